@@ -1,0 +1,15 @@
+"""CPU oracle for UPipe causal GQA attention (test infrastructure only).
+
+This package is the checker, not the product. Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it. It shares no code with the HIP path and never imports it.
+"""
+
+from .attention import (  # noqa: F401
+    attention_forward,
+    attention_backward,
+    forward_rows,
+    backward_rows_dq,
+    backward_cols_dkdv,
+    kv_head_of,
+)

@@ -1,0 +1,268 @@
+"""Plain, slow fp64 CPU oracle of exact causal GQA attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY. This module is the checker of the HIP path, not a
+part of it: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it. It shares no code, header,
+table or helper with the HIP library and imports nothing from it.
+
+Sources (web pages, cited by title and section):
+
+[ROAD]  "Road to 5 Million Tokens: Breaking Barriers in Long Context Training"
+        (Max Ryabinin, AI Engineer Europe 2026), talk summary page: sections
+        "Chapters" (the DeepSpeed Ulysses chapter, the chapter on processing
+        heads in batches, the Q&A chapter) and "Glossary" (UPipe, Ulysses).
+[DIGEST] Russian digest of the same talk (transcript digest page): "Quiz"
+        answers on Ulysses and on U-Pipe; "Insights" 02.
+[MAXTEXT] Article on long-context training in MaxText v0.2.4 on Cloud TPU:
+        the release section (attention variants MHA / GQA / MLA; Splash skips
+        fully masked blocks), the section on where long-sequence training gets
+        stuck (each position looks back over all earlier positions), and the
+        strategy-choice table (Ulysses splits heads, not positions).
+
+What the oracle computes. Under Ulysses-style context parallelism a GPU runs
+exact attention for its own heads over the whole sequence [ROAD Chapters,
+Ulysses; DIGEST Quiz, Ulysses]. UPipe only changes *when* those heads run
+(sequential head chunks reusing one buffer) [ROAD Chapters, batched heads;
+DIGEST Quiz, U-Pipe]; it does not change what each head computes. Nothing is
+approximated, so this module writes the definition of attention out, in
+float64, with every input taken as the exact value of its element:
+
+    A(i)   = {0..i} if causal else {0..S-1}            (look-back set)
+    s_ij   = tau * <q_hi, k_gj>,  tau = 1/sqrt(d),  g = kv head of h
+    LSE_hi = log sum_{j in A(i)} exp(s_ij)             (natural log)
+    P_ij   = exp(s_ij - LSE_hi)
+    O_hi   = sum_{j in A(i)} P_ij v_gj
+  backward, given the upstream gradient dO:
+    D_hi   = <dO_hi, O_hi>
+    dP_ij  = <dO_hi, v_gj>
+    dS_ij  = P_ij (dP_ij - D_hi)
+    dQ_hi  = tau sum_j dS_ij k_gj
+    dK_gj  = tau sum_{h in group g} sum_{i: j in A(i)} dS_ij q_hi
+    dV_gj  = sum_{h in group g} sum_{i: j in A(i)} P_ij dO_hi
+
+Readings where the pages are silent or ambiguous:
+  * causal look-back includes the position itself (j <= i);
+  * tau = 1/sqrt(d); LSE is a natural log;
+  * GQA heads are grouped contiguously: q head h reads kv head h // (Hq/Hkv);
+  * layouts: q, k, v, dO, O are [S, H, d] (token-major); LSE is [Hq, S].
+
+Algorithm: row blocks of R query rows; for each block the full score rows are
+formed, then (1) the row max, (2) exp and row sum, (3) the weighted sum of V.
+No online softmax, no tiling of the key axis. numpy matmul is the only library
+primitive used.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "kv_head_of",
+    "attention_forward",
+    "attention_backward",
+    "forward_rows",
+    "backward_rows_dq",
+    "backward_cols_dkdv",
+]
+
+# Upper bound on the number of float64 score elements held at once.
+_SCORE_BUDGET = 1 << 24
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
+    """KV head read by query head ``h`` under GQA (contiguous groups)."""
+    if n_q_heads % n_kv_heads:
+        raise ValueError("query heads must be a multiple of kv heads")
+    return h // (n_q_heads // n_kv_heads)
+
+
+def _look_back_mask(rows: np.ndarray, n_cols: int, causal: bool) -> np.ndarray | None:
+    """True where key j is NOT in A(i) for each row i in ``rows``."""
+    if not causal:
+        return None
+    return np.arange(n_cols)[None, :] > rows[:, None]
+
+
+def _softmax_rows(s: np.ndarray):
+    """Row max, exp and row sum of a score block (masked entries are -inf)."""
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m + np.log(l)
+
+
+def attention_forward(q, k, v, causal: bool = True, block: int = 256):
+    """Full-tensor forward. Returns (out [S,Hq,d], lse [Hq,S]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    tau = 1.0 / math.sqrt(d)
+    out = np.zeros((S, Hq, d))
+    lse = np.zeros((Hq, S))
+    for h in range(Hq):
+        g = kv_head_of(h, Hq, Hkv)
+        for r0 in range(0, S, block):
+            r1 = min(S, r0 + block)
+            rows = np.arange(r0, r1)
+            n_cols = r1 if causal else S
+            s = tau * (q[r0:r1, h, :] @ k[:n_cols, g, :].T)
+            mask = _look_back_mask(rows, n_cols, causal)
+            if mask is not None:
+                s[mask] = -np.inf
+            p, lse_blk = _softmax_rows(s)
+            out[r0:r1, h, :] = p @ v[:n_cols, g, :]
+            lse[h, r0:r1] = lse_blk
+    return out, lse
+
+
+def attention_backward(q, k, v, dout, causal: bool = True, block: int = 256):
+    """Full-tensor backward. Returns (dq, dk, dv) in float64, shaped like q, k, v.
+
+    P is recomputed from the exact forward's LSE; D uses the exact O.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    tau = 1.0 / math.sqrt(d)
+    out, lse = attention_forward(q, k, v, causal, block)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(Hq):
+        g = kv_head_of(h, Hq, Hkv)
+        for r0 in range(0, S, block):
+            r1 = min(S, r0 + block)
+            rows = np.arange(r0, r1)
+            n_cols = r1 if causal else S
+            q_blk = q[r0:r1, h, :]
+            do_blk = dout[r0:r1, h, :]
+            s = tau * (q_blk @ k[:n_cols, g, :].T)
+            mask = _look_back_mask(rows, n_cols, causal)
+            if mask is not None:
+                s[mask] = -np.inf
+            p = np.exp(s - lse[h, r0:r1][:, None])
+            dp = do_blk @ v[:n_cols, g, :].T
+            D = (do_blk * out[r0:r1, h, :]).sum(axis=1)
+            ds = p * (dp - D[:, None])
+            dq[r0:r1, h, :] = tau * (ds @ k[:n_cols, g, :])
+            dk[:n_cols, g, :] += tau * (ds.T @ q_blk)
+            dv[:n_cols, g, :] += p.T @ do_blk
+    return dq, dk, dv
+
+
+def _row_batches(rows: np.ndarray, S: int, causal: bool):
+    """Split sorted row indices into batches whose score block fits the budget."""
+    order = np.argsort(rows, kind="stable")
+    start, n = 0, len(order)
+    while start < n:
+        end = start + 1
+        while end < n:
+            width = int(rows[order[end]]) + 1 if causal else S
+            if (end - start + 1) * width > _SCORE_BUDGET:
+                break
+            end += 1
+        yield order[start:end]
+        start = end
+
+
+def forward_rows(q, k, v, rows, causal: bool = True):
+    """Exact O and LSE at selected query rows, O(S*d) work per row.
+
+    Returns (out_rows [R,Hq,d], lse_rows [Hq,R]) in float64, in ``rows`` order.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    rows = np.asarray(rows, dtype=np.int64)
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    tau = 1.0 / math.sqrt(d)
+    out = np.zeros((len(rows), Hq, d))
+    lse = np.zeros((Hq, len(rows)))
+    for sel in _row_batches(rows, S, causal):
+        r = rows[sel]
+        n_cols = int(r.max()) + 1 if causal else S
+        mask = _look_back_mask(r, n_cols, causal)
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            s = tau * (q[r, h, :] @ k[:n_cols, g, :].T)
+            if mask is not None:
+                s[mask] = -np.inf
+            p, lse_blk = _softmax_rows(s)
+            out[sel, h, :] = p @ v[:n_cols, g, :]
+            lse[h, sel] = lse_blk
+    return out, lse
+
+
+def backward_rows_dq(q, k, v, dout, rows, causal: bool = True):
+    """Exact dQ at selected query rows, O(S*d) work per row.
+
+    D_hi needs only row i's own O, so each row is self-contained.
+    Returns dq_rows [R,Hq,d] in float64, in ``rows`` order.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    rows = np.asarray(rows, dtype=np.int64)
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    tau = 1.0 / math.sqrt(d)
+    dq = np.zeros((len(rows), Hq, d))
+    for sel in _row_batches(rows, S, causal):
+        r = rows[sel]
+        n_cols = int(r.max()) + 1 if causal else S
+        mask = _look_back_mask(r, n_cols, causal)
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            s = tau * (q[r, h, :] @ k[:n_cols, g, :].T)
+            if mask is not None:
+                s[mask] = -np.inf
+            p, _ = _softmax_rows(s)
+            o = p @ v[:n_cols, g, :]
+            D = (dout[r, h, :] * o).sum(axis=1)
+            dp = dout[r, h, :] @ v[:n_cols, g, :].T
+            ds = p * (dp - D[:, None])
+            dq[sel, h, :] = tau * (ds @ k[:n_cols, g, :])
+    return dq
+
+
+def backward_cols_dkdv(q, k, v, dout, cols, causal: bool = True):
+    """Exact dK and dV at selected key rows, from the inputs alone.
+
+    Key j collects from every row i with j in A(i): i >= j when causal, every
+    row otherwise. Each such row's LSE and O come from :func:`forward_rows`, so
+    the cost is O(|rows| * S * d), which is small when the keys lie near the
+    end of a causal sequence. Returns (dk_cols [C,Hkv,d], dv_cols [C,Hkv,d]).
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cols = np.asarray(cols, dtype=np.int64)
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    tau = 1.0 / math.sqrt(d)
+    first = int(cols.min()) if causal else 0
+    need = np.arange(first, S)
+    o_need, lse_need = forward_rows(q, k, v, need, causal)
+    dk = np.zeros((len(cols), Hkv, d))
+    dv = np.zeros((len(cols), Hkv, d))
+    n_rows = len(need)
+    per = max(1, _SCORE_BUDGET // max(1, n_rows))
+    for c0 in range(0, len(cols), per):
+        cj = cols[c0:c0 + per]
+        # row i (absolute index need[t]) contributes to key j only if j in A(i)
+        excluded = (need[None, :] < cj[:, None]) if causal else None
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            qh = q[need, h, :]
+            doh = dout[need, h, :]
+            s = tau * (k[cj, g, :] @ qh.T)  # [C, n_rows] = s_ij transposed
+            p = np.exp(s - lse_need[h][None, :])
+            if excluded is not None:
+                p[excluded] = 0.0
+            D = (doh * o_need[:, h, :]).sum(axis=1)
+            dp = v[cj, g, :] @ doh.T
+            ds = p * (dp - D[None, :])
+            dk[c0:c0 + per, g, :] += tau * (ds @ qh)
+            dv[c0:c0 + per, g, :] += p @ doh
+    return dk, dv

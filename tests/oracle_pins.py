@@ -1,0 +1,237 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each pin takes an oracle *module* (the real ``oracle.attention`` or a copy
+with a planted mistake) and raises AssertionError when the oracle disagrees
+with: a library routine (torch's fp64 scaled_dot_product_attention and its
+autograd), central finite differences, a closed form, or an identity that the
+mathematics of softmax attention fixes. None of them retypes the oracle's
+formulas.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+RNG_SEED = 1234
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _sdpa(q, k, v, causal):
+    """torch fp64 SDPA on [S,H,d] arrays with contiguous GQA groups."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    G = Hq // Hkv
+    tq = torch.tensor(q).permute(1, 0, 2).unsqueeze(0)
+    tk = torch.tensor(k).permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0)
+    tv = torch.tensor(v).permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0)
+    return tq, tk, tv
+
+
+def pin_sdpa_forward(mod, S=37, Hq=4, Hkv=2, d=16, causal=True):
+    q, k, v = _rand((S, Hq, d), 1), _rand((S, Hkv, d), 2), _rand((S, Hkv, d), 3)
+    out, lse = mod.attention_forward(q, k, v, causal=causal, block=8)
+    tq, tk, tv = _sdpa(q, k, v, causal)
+    ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
+    ref = ref.squeeze(0).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+    # LSE: log of the softmax denominator, from a library logsumexp
+    s = torch.einsum("hid,hjd->hij", tq[0], tk[0]) / math.sqrt(d)
+    if causal:
+        s = s.masked_fill(torch.ones(S, S, dtype=torch.bool).triu(1), float("-inf"))
+    ref_lse = torch.logsumexp(s, dim=-1).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def pin_sdpa_backward(mod, S=29, Hq=4, Hkv=2, d=8, causal=True):
+    q, k, v = _rand((S, Hq, d), 4), _rand((S, Hkv, d), 5), _rand((S, Hkv, d), 6)
+    do = _rand((S, Hq, d), 7)
+    dq, dk, dv = mod.attention_backward(q, k, v, do, causal=causal, block=8)
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    G = Hq // Hkv
+    o = F.scaled_dot_product_attention(
+        tq.permute(1, 0, 2).unsqueeze(0),
+        tk.permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0),
+        tv.permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0),
+        is_causal=causal,
+    ).squeeze(0).permute(1, 0, 2)
+    o.backward(torch.tensor(do))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def pin_finite_differences(mod, S=6, Hq=2, Hkv=1, d=3, causal=True, eps=1e-6):
+    """Central differences of f = sum(dO * O) against the analytic gradients."""
+    q, k, v = _rand((S, Hq, d), 8), _rand((S, Hkv, d), 9), _rand((S, Hkv, d), 10)
+    do = _rand((S, Hq, d), 11)
+    dq, dk, dv = mod.attention_backward(q, k, v, do, causal=causal, block=4)
+
+    def f(qq, kk, vv):
+        o, _ = mod.attention_forward(qq, kk, vv, causal=causal, block=4)
+        return float((do * o).sum())
+
+    def f_with(name, xx):
+        args = {"q": q, "k": k, "v": v}
+        args[name] = xx
+        return f(args["q"], args["k"], args["v"])
+
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            num[idx] = (f_with(name, xp) - f_with(name, xm)) / (2 * eps)
+        err = np.abs(num - g).max() / max(1e-12, np.abs(g).max())
+        assert err < 1e-6, f"finite differences disagree on d{name}: rel {err:.2e}"
+
+
+def pin_row0_closed_form(mod, S=11, Hq=3, Hkv=1, d=8):
+    """Causal row 0 sees only key 0: O_0 = v_0 and LSE_0 = <q_0,k_0>/sqrt(d)."""
+    q, k, v = _rand((S, Hq, d), 12), _rand((S, Hkv, d), 13), _rand((S, Hkv, d), 14)
+    out, lse = mod.attention_forward(q, k, v, causal=True)
+    for h in range(Hq):
+        np.testing.assert_allclose(out[0, h], v[0, 0], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(lse[h, 0], q[0, h] @ k[0, 0] / math.sqrt(d), rtol=1e-14)
+
+
+def pin_uniform_keys(mod, S=19, Hq=2, Hkv=1, d=8):
+    """All keys equal: scores are constant along each row, so O_i is the mean of
+    v_0..v_i and LSE_i = <q_i,c>/sqrt(d) + ln(i+1)."""
+    q, v = _rand((S, Hq, d), 15), _rand((S, Hkv, d), 16)
+    c = _rand((d,), 17)
+    k = np.broadcast_to(c, (S, Hkv, d)).copy()
+    out, lse = mod.attention_forward(q, k, v, causal=True, block=5)
+    means = np.cumsum(v[:, 0, :], axis=0) / np.arange(1, S + 1)[:, None]
+    for h in range(Hq):
+        np.testing.assert_allclose(out[:, h, :], means, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse[h], q[:, h, :] @ c / math.sqrt(d) + np.log(np.arange(1, S + 1)),
+                                   rtol=1e-12, atol=1e-13)
+    # q = 0 gives the same uniform weights whatever the keys
+    k2 = _rand((S, Hkv, d), 18)
+    out0, lse0 = mod.attention_forward(np.zeros_like(q), k2, v, causal=True, block=7)
+    np.testing.assert_allclose(out0[:, 0, :], means, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse0[0], np.log(np.arange(1, S + 1)), rtol=1e-12, atol=1e-13)
+
+
+def pin_ones_values(mod, S=23, Hq=2, Hkv=2, d=4):
+    """Softmax rows sum to one, so V = 1 gives O = 1 (causal and not)."""
+    q, k = _rand((S, Hq, d), 19) * 3, _rand((S, Hkv, d), 20) * 3
+    v = np.ones((S, Hkv, d))
+    for causal in (True, False):
+        out, _ = mod.attention_forward(q, k, v, causal=causal, block=6)
+        np.testing.assert_allclose(out, 1.0, rtol=1e-13)
+
+
+def pin_last_row_noncausal(mod, S=17, Hq=2, Hkv=1, d=8):
+    """The last causal row sees every key, so it equals the non-causal row."""
+    q, k, v = _rand((S, Hq, d), 21), _rand((S, Hkv, d), 22), _rand((S, Hkv, d), 23)
+    oc, lc = mod.attention_forward(q, k, v, causal=True)
+    on, ln = mod.attention_forward(q, k, v, causal=False)
+    np.testing.assert_allclose(oc[-1], on[-1], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lc[:, -1], ln[:, -1], rtol=1e-13)
+    assert np.abs(oc[0] - on[0]).max() > 1e-3  # row 0 does differ
+
+
+def pin_gradient_sums(mod, S=21, Hq=4, Hkv=2, d=8, causal=True):
+    """sum_j dK_j = 0 (softmax is blind to a shift of every key) and
+    sum_j dV_j = sum over the group's heads and all rows of dO (rows of P sum
+    to one)."""
+    q, k, v = _rand((S, Hq, d), 24), _rand((S, Hkv, d), 25), _rand((S, Hkv, d), 26)
+    do = _rand((S, Hq, d), 27)
+    _, dk, dv = mod.attention_backward(q, k, v, do, causal=causal, block=5)
+    G = Hq // Hkv
+    for g in range(Hkv):
+        np.testing.assert_allclose(dk[:, g, :].sum(axis=0), 0.0, atol=1e-12)
+        ref = do[:, g * G:(g + 1) * G, :].sum(axis=(0, 1))
+        np.testing.assert_allclose(dv[:, g, :].sum(axis=0), ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_key_shift(mod, S=15, Hq=2, Hkv=1, d=8):
+    """k_j -> k_j + c adds a per-row constant to the scores: O, dQ, dK, dV are
+    unchanged and LSE_i moves by <q_i,c>/sqrt(d)."""
+    q, k, v = _rand((S, Hq, d), 28), _rand((S, Hkv, d), 29), _rand((S, Hkv, d), 30)
+    do = _rand((S, Hq, d), 31)
+    c = _rand((d,), 32)
+    o1, l1 = mod.attention_forward(q, k, v)
+    o2, l2 = mod.attention_forward(q, k + c, v)
+    np.testing.assert_allclose(o1, o2, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(l2 - l1, (q @ c).T / math.sqrt(d), rtol=1e-11, atol=1e-12)
+    g1 = mod.attention_backward(q, k, v, do)
+    g2 = mod.attention_backward(q, k + c, v, do)
+    for a, b in zip(g1, g2):
+        np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-11)
+
+
+def pin_gqa_equals_repeated_mha(mod, S=13, Hq=6, Hkv=2, d=4):
+    """GQA equals MHA with each kv head repeated over its group of Hq/Hkv
+    consecutive query heads; dK/dV are the group sums of the MHA ones."""
+    q, k, v = _rand((S, Hq, d), 33), _rand((S, Hkv, d), 34), _rand((S, Hkv, d), 35)
+    do = _rand((S, Hq, d), 36)
+    G = Hq // Hkv
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    og, lg = mod.attention_forward(q, k, v)
+    om, lm = mod.attention_forward(q, kr, vr)
+    np.testing.assert_allclose(og, om, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lg, lm, rtol=1e-13, atol=1e-14)
+    dqg, dkg, dvg = mod.attention_backward(q, k, v, do)
+    dqm, dkm, dvm = mod.attention_backward(q, kr, vr, do)
+    np.testing.assert_allclose(dqg, dqm, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dkg, dkm.reshape(S, Hkv, G, d).sum(axis=2), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dvg, dvm.reshape(S, Hkv, G, d).sum(axis=2), rtol=1e-12, atol=1e-13)
+
+
+def pin_sampled_functions(mod, S=53, Hq=4, Hkv=1, d=8):
+    """The O(S*d)-per-row functions agree with the full-tensor ones (which the
+    other pins tie to torch and to finite differences)."""
+    q, k, v = _rand((S, Hq, d), 37), _rand((S, Hkv, d), 38), _rand((S, Hkv, d), 39)
+    do = _rand((S, Hq, d), 40)
+    for causal in (True, False):
+        out, lse = mod.attention_forward(q, k, v, causal=causal, block=9)
+        dq, dk, dv = mod.attention_backward(q, k, v, do, causal=causal, block=9)
+        # one sample with the last row, one that stays in the first half
+        for rows in (np.array([0, 1, 7, 8, 31, 52, 20]), np.array([3, 0, 11, 25])):
+            o_r, l_r = mod.forward_rows(q, k, v, rows, causal=causal)
+            np.testing.assert_allclose(o_r, out[rows], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(l_r, lse[:, rows], rtol=1e-12, atol=1e-13)
+            dq_r = mod.backward_rows_dq(q, k, v, do, rows, causal=causal)
+            np.testing.assert_allclose(dq_r, dq[rows], rtol=1e-11, atol=1e-12)
+        cols = np.array([52, 40, 45, 3]) if not causal else np.array([52, 40, 45])
+        dk_c, dv_c = mod.backward_cols_dkdv(q, k, v, do, cols, causal=causal)
+        np.testing.assert_allclose(dk_c, dk[cols], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dv_c, dv[cols], rtol=1e-11, atol=1e-12)
+
+
+ALL_PINS = [
+    pin_sdpa_forward,
+    pin_sdpa_backward,
+    pin_finite_differences,
+    pin_row0_closed_form,
+    pin_uniform_keys,
+    pin_ones_values,
+    pin_last_row_noncausal,
+    pin_gradient_sums,
+    pin_key_shift,
+    pin_gqa_equals_repeated_mha,
+    pin_sampled_functions,
+]
+
+
+def failing_pins(mod):
+    """Names of the pins that ``mod`` fails (an exception of any kind counts)."""
+    bad = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception:  # noqa: BLE001 - a crash is a failed pin too
+            bad.append(pin.__name__)
+    return bad

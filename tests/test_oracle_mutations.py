@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in a copy of the oracle (CPU only) and check that
+at least one pin catches each: the pins are strong enough to trust."""
+
+import importlib.util
+import os
+import types
+
+import pytest
+
+from oracle_pins import failing_pins
+
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTATIONS = {
+    "scale_1_over_d": ("tau = 1.0 / math.sqrt(d)", "tau = 1.0 / d"),
+    "diagonal_excluded": ("np.arange(n_cols)[None, :] > rows[:, None]", "np.arange(n_cols)[None, :] >= rows[:, None]"),
+    "gqa_modulo_mapping": ("return h // (n_q_heads // n_kv_heads)", "return h % n_kv_heads"),
+    "lse_base2": ("return e / l[:, None], m + np.log(l)", "return e / l[:, None], m + np.log2(l)"),
+    "lse_missing_max": ("return e / l[:, None], m + np.log(l)", "return e / l[:, None], np.log(l)"),
+    "bwd_missing_D": ("ds = p * (dp - D[:, None])", "ds = p * dp"),
+    "bwd_dk_missing_tau": ("dk[:n_cols, g, :] += tau * (ds.T @ q_blk)", "dk[:n_cols, g, :] += (ds.T @ q_blk)"),
+    "bwd_dv_uses_ds": ("dv[:n_cols, g, :] += p.T @ do_blk", "dv[:n_cols, g, :] += ds.T @ do_blk"),
+    "bwd_dq_transposed_k": ("dq[r0:r1, h, :] = tau * (ds @ k[:n_cols, g, :])", "dq[r0:r1, h, :] = tau * (ds @ v[:n_cols, g, :])"),
+    "rows_dq_missing_D": ("ds = p * (dp - D[:, None])\n            dq[sel", "ds = p * dp\n            dq[sel"),
+    "cols_wrong_causal_side": ("(need[None, :] < cj[:, None])", "(need[None, :] > cj[:, None])"),
+    "cols_dv_missing": ("dv[c0:c0 + per, g, :] += p @ doh", "dv[c0:c0 + per, g, :] += 0 * (p @ doh)"),
+    "fwd_rows_noncausal_width": ("n_cols = int(r.max()) + 1 if causal else S\n        mask = _look_back_mask(r, n_cols, causal)\n        for h in range(Hq):\n            g = kv_head_of(h, Hq, Hkv)\n            s = tau * (q[r, h, :] @ k[:n_cols, g, :].T)\n            if mask is not None:\n                s[mask] = -np.inf\n            p, lse_blk",
+                                 "n_cols = int(r.max()) + 1\n        mask = _look_back_mask(r, n_cols, causal)\n        for h in range(Hq):\n            g = kv_head_of(h, Hq, Hkv)\n            s = tau * (q[r, h, :] @ k[:n_cols, g, :].T)\n            if mask is not None:\n                s[mask] = -np.inf\n            p, lse_blk"),
+}
+
+
+def _mutant(old, new):
+    with open(SRC_PATH) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new, 1)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant.py", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    old, new = MUTATIONS[name]
+    bad = failing_pins(_mutant(old, new))
+    assert bad, f"no pin catches the planted mistake {name}"
+
+
+def test_unmutated_copy_passes_every_pin():
+    with open(SRC_PATH) as f:
+        src = f.read()
+    mod = types.ModuleType("oracle_copy")
+    exec(compile(src, "oracle_copy.py", "exec"), mod.__dict__)
+    assert failing_pins(mod) == []
