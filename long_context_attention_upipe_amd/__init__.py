@@ -1,0 +1,59 @@
+"""UPipe causal GQA attention for MI355X (gfx950).
+
+The compute path is the HIP library ``libupipe_attn.so`` behind the C ABI in
+``include/upipe_attn.h``; this package only binds it (``_lib``) and adds thin
+helpers that let torch allocate the outputs and the fixed buffer pool.
+"""
+
+from ._lib import (  # noqa: F401
+    UPIPE_BF16,
+    UPIPE_FP32,
+    UpipeError,
+    dtype_code,
+    upipe_attn_bwd,
+    upipe_attn_bwd_workspace_bytes,
+    upipe_attn_fwd,
+    upipe_attn_fwd_workspace_bytes,
+    upipe_attn_plan,
+    upipe_last_error,
+)
+
+
+def workspace(S, Hq, Hkv, d, head_chunk, dtype, device="cuda", which="both"):
+    """Allocate the fixed buffer pool (uint8) for the forward, backward or both."""
+    import torch
+
+    code = dtype_code(dtype) if not isinstance(dtype, int) else dtype
+    sizes = []
+    if which in ("fwd", "both"):
+        sizes.append(upipe_attn_fwd_workspace_bytes(S, Hq, Hkv, d, head_chunk, code))
+    if which in ("bwd", "both"):
+        sizes.append(upipe_attn_bwd_workspace_bytes(S, Hq, Hkv, d, head_chunk, code))
+    return torch.empty(max(sizes), dtype=torch.uint8, device=device)
+
+
+def attention_forward(q, k, v, head_chunk=1, causal=True, ws=None, stream=None):
+    """out, lse = attention over [S,Hq,d] / [S,Hkv,d] device tensors."""
+    import torch
+
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    out = torch.empty_like(q)
+    lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(S, Hq, Hkv, d, head_chunk, q.dtype, q.device, "fwd")
+    upipe_attn_fwd(q, k, v, out, lse, head_chunk, causal, ws, stream)
+    return out, lse
+
+
+def attention_backward(q, k, v, out, dout, lse, head_chunk=1, causal=True, ws=None, stream=None):
+    """dq, dk, dv of attention given the forward's out and lse."""
+    import torch
+
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if ws is None:
+        ws = workspace(S, Hq, Hkv, d, head_chunk, q.dtype, q.device, "bwd")
+    upipe_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, head_chunk, causal, ws, stream)
+    return dq, dk, dv

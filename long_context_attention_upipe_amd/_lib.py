@@ -1,0 +1,150 @@
+"""ctypes binding of libupipe_attn.so (C ABI declared in include/upipe_attn.h).
+
+Argument marshalling only: torch supplies device memory (``data_ptr``) and the
+stream handle; every step of the computation runs in the library's HIP
+kernels. There is no fallback: if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_NAME = "libupipe_attn.so"
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, _LIB_NAME)
+
+UPIPE_BF16 = 0
+UPIPE_FP32 = 1
+STATUS = {0: "UPIPE_OK", -1: "UPIPE_EINVAL", -2: "UPIPE_EUNSUPPORTED", -3: "UPIPE_EWORKSPACE", -4: "UPIPE_EHIP"}
+
+_lib = None
+
+
+class UpipeError(RuntimeError):
+    """A negative status from the library, with its message."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(there is no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, sz, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    L.upipe_attn_fwd_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.upipe_attn_fwd_workspace_bytes.restype = sz
+    L.upipe_attn_bwd_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.upipe_attn_bwd_workspace_bytes.restype = sz
+    L.upipe_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.upipe_attn_fwd.restype = i32
+    L.upipe_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.upipe_attn_bwd.restype = i32
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    L.upipe_attn_plan.argtypes = [i32, i32, i32, i32, p32, p32, p32, p32]
+    L.upipe_attn_plan.restype = i32
+    L.upipe_last_error.argtypes = []
+    L.upipe_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def upipe_last_error() -> str:
+    return lib().upipe_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise UpipeError(status, upipe_last_error())
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return UPIPE_BF16
+    if dt == torch.float32:
+        return UPIPE_FP32
+    raise UpipeError(-2, f"unsupported dtype {dt}")
+
+
+def upipe_attn_fwd_workspace_bytes(S, Hq, Hkv, d, head_chunk, dtype) -> int:
+    n = lib().upipe_attn_fwd_workspace_bytes(S, Hq, Hkv, d, head_chunk, dtype)
+    if n == 0:
+        raise UpipeError(-1, upipe_last_error())
+    return n
+
+
+def upipe_attn_bwd_workspace_bytes(S, Hq, Hkv, d, head_chunk, dtype) -> int:
+    n = lib().upipe_attn_bwd_workspace_bytes(S, Hq, Hkv, d, head_chunk, dtype)
+    if n == 0:
+        raise UpipeError(-1, upipe_last_error())
+    return n
+
+
+def upipe_attn_plan(Hq, Hkv, head_chunk):
+    """The head-chunk plan as a list of dicts (host only)."""
+    n = max(1, Hq)
+    arrs = [(ctypes.c_int32 * n)() for _ in range(4)]
+    rc = lib().upipe_attn_plan(Hq, Hkv, head_chunk, n, *arrs)
+    if rc < 0:
+        raise UpipeError(rc, upipe_last_error())
+    return [dict(q_head0=arrs[0][i], kv_head0=arrs[1][i], n_kv=arrs[2][i],
+                 load_kv=bool(arrs[3][i] & 1), first_for_kv=bool(arrs[3][i] & 2),
+                 last_for_kv=bool(arrs[3][i] & 4)) for i in range(rc)]
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _shape(q, k):
+    if q.dim() != 3 or k.dim() != 3:
+        raise UpipeError(-1, "q and k must be [S, H, d]")
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    return S, Hq, Hkv, d
+
+
+def _require(ts, dt):
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise UpipeError(-1, "tensors must be contiguous device tensors")
+        if t.dtype != dt:
+            raise UpipeError(-1, f"dtype mismatch: {t.dtype} vs {dt}")
+
+
+def upipe_attn_fwd(q, k, v, out, lse, head_chunk, causal, workspace, stream=None) -> None:
+    """Enqueue the forward on ``stream`` (default: torch's current stream)."""
+    S, Hq, Hkv, d = _shape(q, k)
+    _require((q, k, v, out), q.dtype)
+    _require((lse,), torch.float32)
+    _require((workspace,), torch.uint8)
+    _check(lib().upipe_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), S, Hq, Hkv, d,
+                                int(head_chunk), int(causal), dtype_code(q.dtype),
+                                _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+
+
+def upipe_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, head_chunk, causal, workspace, stream=None) -> None:
+    """Enqueue the backward on ``stream`` (default: torch's current stream)."""
+    S, Hq, Hkv, d = _shape(q, k)
+    _require((q, k, v, out, dout, dq, dk, dv), q.dtype)
+    _require((lse,), torch.float32)
+    _require((workspace,), torch.uint8)
+    _check(lib().upipe_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                                _ptr(dq), _ptr(dk), _ptr(dv), S, Hq, Hkv, d,
+                                int(head_chunk), int(causal), dtype_code(q.dtype),
+                                _ptr(workspace), workspace.numel(), _stream_handle(stream)))

@@ -1,0 +1,73 @@
+// HBM-bound helper kernels around the attention kernels.
+//
+//  * pack / unpack: move a head chunk between the caller's token-major
+//    [S, H, d] tensors and the pool's head-major [hc, S, d] buffers. On one
+//    GPU this copy stands in for the Ulysses all-to-all that would bring the
+//    chunk's heads, over the whole sequence, into the reused buffer
+//    ("Road to 5 Million Tokens" talk summary, Chapters: Ulysses exchanges
+//    activations between GPUs; batched heads reuse the previous batch's
+//    buffer).
+//  * bwd_pre: D_i = <dO_i, O_i> per row in fp32 from the stored output, and
+//    the chunk's dO rows packed in the same pass.
+#pragma once
+
+#include "common.hpp"
+
+namespace upipe {
+
+// dst[hl][i][:] = src[i][h0 + hl][:]  (vpr = 16-byte vectors per row).
+__global__ __launch_bounds__(256) void pack_heads_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                        int S, int H, int h0, int nh, int vpr) {
+  const uint32_t total = (uint32_t)S * (uint32_t)nh * (uint32_t)vpr;
+  for (uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
+    const uint32_t v = idx % vpr;
+    const uint32_t r = idx / vpr;
+    const uint32_t hl = r % nh;
+    const uint32_t i = r / nh;
+    dst[((size_t)hl * S + i) * vpr + v] = src[((size_t)i * H + h0 + hl) * vpr + v];
+  }
+}
+
+// dst[i][h0 + hl][:] = src[hl][i][:]
+__global__ __launch_bounds__(256) void unpack_heads_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                          int S, int H, int h0, int nh, int vpr) {
+  const uint32_t total = (uint32_t)S * (uint32_t)nh * (uint32_t)vpr;
+  for (uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
+    const uint32_t v = idx % vpr;
+    const uint32_t r = idx / vpr;
+    const uint32_t hl = r % nh;
+    const uint32_t i = r / nh;
+    dst[((size_t)i * H + h0 + hl) * vpr + v] = src[((size_t)hl * S + i) * vpr + v];
+  }
+}
+
+// One group of D/EPV lanes per (row, head): reads a 16-byte slice of out and
+// dout each, writes the dout slice into the pool, reduces the dot product.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out, const T* __restrict__ dout,
+                                                     T* __restrict__ dout_pool, float* __restrict__ Drow,
+                                                     int S, int H, int h0, int nh) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int TPR = D / EPV;  // lanes per row: 16 (bf16, d=128), 8, 16 or 32
+  constexpr int RPB = 256 / TPR;
+  const int sub = threadIdx.x % TPR;
+  const uint32_t total = (uint32_t)S * (uint32_t)nh;
+  for (uint32_t r = blockIdx.x * RPB + threadIdx.x / TPR; r < total; r += gridDim.x * RPB) {
+    const uint32_t hl = r % nh;
+    const uint32_t i = r / nh;
+    const size_t src = ((size_t)i * H + h0 + hl) * D + sub * EPV;
+    const uint4 ov = *reinterpret_cast<const uint4*>(out + src);
+    const uint4 dv = *reinterpret_cast<const uint4*>(dout + src);
+    *reinterpret_cast<uint4*>(dout_pool + ((size_t)hl * S + i) * D + sub * EPV) = dv;
+    const T* oe = reinterpret_cast<const T*>(&ov);
+    const T* de = reinterpret_cast<const T*>(&dv);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc = fmaf(to_f32(oe[e]), to_f32(de[e]), acc);
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (sub == 0) Drow[(size_t)hl * S + i] = acc;
+  }
+}
+
+}  // namespace upipe

@@ -1,0 +1,360 @@
+// Host runtime and C ABI of the UPipe attention library (declared in
+// include/upipe_attn.h): argument validation, the head-chunk planner, the
+// layout of the fixed buffer pool, and the per-chunk launch sequence.
+//
+// UPipe ("Road to 5 Million Tokens" talk summary, Chapters: heads processed
+// in batches; talk digest, Quiz answer on U-Pipe): one group of heads already
+// fills the GPU, so the GPU's heads run as sequential chunks and every chunk
+// reuses the buffers the previous chunk used. Here the buffers are one
+// caller-provided workspace carved at fixed offsets; nothing is allocated
+// inside the chunk loop, and peak memory grows with head_chunk only.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/upipe_attn.h"
+#include "attn_bwd.hpp"
+#include "attn_fwd.hpp"
+#include "copy_kernels.hpp"
+
+namespace upipe {
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Problem {
+  int64_t S;
+  int Hq, Hkv, d, hc, causal, dtype;
+  int G;             // q heads per kv head
+  int heads_per_kv;  // q heads of one chunk that share a kv head = min(hc, G)
+  int nkv;           // kv heads one chunk reads = max(1, hc / G)
+  size_t es;         // element size
+};
+
+int validate(int64_t S, int Hq, int Hkv, int d, int hc, int causal, int dtype, Problem* pr) {
+  if (S < 1) return fail(UPIPE_EINVAL, "S must be >= 1 (got %lld)", (long long)S);
+  if (Hq < 1 || Hkv < 1) return fail(UPIPE_EINVAL, "Hq and Hkv must be >= 1 (got %d, %d)", Hq, Hkv);
+  if (Hq % Hkv) return fail(UPIPE_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (hc < 1 || Hq % hc) return fail(UPIPE_EINVAL, "head_chunk (%d) must divide Hq (%d)", hc, Hq);
+  const int G = Hq / Hkv;
+  if (!(G % hc == 0 || hc % G == 0))
+    return fail(UPIPE_EINVAL, "head_chunk (%d) must divide or be a multiple of Hq/Hkv (%d)", hc, G);
+  if (causal != 0 && causal != 1) return fail(UPIPE_EINVAL, "causal must be 0 or 1 (got %d)", causal);
+  if (dtype != UPIPE_BF16 && dtype != UPIPE_FP32) return fail(UPIPE_EUNSUPPORTED, "unsupported dtype %d", dtype);
+  if (d != 64 && d != 128) return fail(UPIPE_EUNSUPPORTED, "unsupported head dim %d (64 or 128)", d);
+  const size_t es = dtype == UPIPE_BF16 ? 2 : 4;
+  if ((uint64_t)S * (uint64_t)d >= (1ull << 31))
+    return fail(UPIPE_EUNSUPPORTED, "S*d must be < 2^31 (S=%lld, d=%d)", (long long)S, d);
+  if ((uint64_t)S * (uint64_t)std::max(Hq, Hkv) * (uint64_t)d * es / 16 >= (1ull << 32))
+    return fail(UPIPE_EUNSUPPORTED, "tensor too large for 32-bit vector indexing");
+  pr->S = S;
+  pr->Hq = Hq;
+  pr->Hkv = Hkv;
+  pr->d = d;
+  pr->hc = hc;
+  pr->causal = causal;
+  pr->dtype = dtype;
+  pr->G = G;
+  pr->heads_per_kv = std::min(hc, G);
+  pr->nkv = std::max(1, hc / G);
+  pr->es = es;
+  return UPIPE_OK;
+}
+
+struct Chunk {
+  int q_head0, kv_head0, n_kv;
+  bool load_kv, first_for_kv, last_for_kv;
+};
+
+// Chunks in ascending head order. A chunk reads the kv heads of its query
+// heads; when head_chunk < G several chunks share one kv head, which is then
+// loaded once and its dK/dV summed over those chunks.
+std::vector<Chunk> plan(const Problem& pr) {
+  std::vector<Chunk> out;
+  int prev_kv = -1;
+  for (int h0 = 0; h0 < pr.Hq; h0 += pr.hc) {
+    Chunk c;
+    c.q_head0 = h0;
+    c.kv_head0 = h0 / pr.G;
+    c.n_kv = pr.nkv;
+    c.load_kv = c.kv_head0 != prev_kv;
+    c.first_for_kv = (h0 % pr.G) == 0;
+    c.last_for_kv = ((h0 + pr.hc) % pr.G) == 0 || pr.hc >= pr.G;
+    prev_kv = c.kv_head0;
+    out.push_back(c);
+  }
+  return out;
+}
+
+// Pool layouts. Every chunk overwrites the same offsets.
+struct FwdPool {
+  size_t q, o, k, v, total;
+};
+FwdPool fwd_pool(const Problem& pr) {
+  const size_t U = (size_t)pr.S * pr.d * pr.es;  // one head, whole sequence
+  FwdPool p;
+  size_t off = 0;
+  p.q = off; off += align_up(pr.hc * U);
+  p.o = off; off += align_up(pr.hc * U);
+  p.k = off; off += align_up(pr.nkv * U);
+  p.v = off; off += align_up(pr.nkv * U);
+  p.total = off;
+  return p;
+}
+
+struct BwdPool {
+  size_t q, dout, dq, k, v, drow, dk_acc, dv_acc, total;
+  bool has_acc;
+};
+BwdPool bwd_pool(const Problem& pr) {
+  const size_t U = (size_t)pr.S * pr.d * pr.es;
+  BwdPool p;
+  size_t off = 0;
+  p.q = off; off += align_up(pr.hc * U);
+  p.dout = off; off += align_up(pr.hc * U);
+  p.dq = off; off += align_up(pr.hc * U);
+  p.k = off; off += align_up(pr.nkv * U);
+  p.v = off; off += align_up(pr.nkv * U);
+  p.drow = off; off += align_up((size_t)pr.hc * pr.S * 4);
+  p.has_acc = pr.hc < pr.G;
+  const size_t A = (size_t)pr.S * pr.d * 4;
+  p.dk_acc = off; off += p.has_acc ? align_up(A) : 0;
+  p.dv_acc = off; off += p.has_acc ? align_up(A) : 0;
+  p.total = off;
+  return p;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+unsigned copy_grid(size_t vectors) {
+  const size_t blocks = (vectors + 255) / 256;
+  return (unsigned)std::min<size_t>(std::max<size_t>(blocks, 1), 256 * 32);
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(UPIPE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return UPIPE_OK;
+}
+
+template <typename T, int D>
+int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* out, float* lse, char* ws,
+            hipStream_t st) {
+  const FwdPool pool = fwd_pool(pr);
+  const int S = (int)pr.S;
+  const int vpr = D * (int)sizeof(T) / 16;
+  T* Qc = reinterpret_cast<T*>(ws + pool.q);
+  T* Oc = reinterpret_cast<T*>(ws + pool.o);
+  T* Kc = reinterpret_cast<T*>(ws + pool.k);
+  T* Vc = reinterpret_cast<T*>(ws + pool.v);
+  const int n_qtiles = (S + FwdShape<T, D>::BQ - 1) / FwdShape<T, D>::BQ;
+  const float scale = 1.0f / std::sqrt((float)D);
+  for (const Chunk& c : plan(pr)) {
+    if (c.load_kv) {
+      const size_t nv = (size_t)S * c.n_kv * vpr;
+      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)k, (uint4*)Kc, S,
+                         pr.Hkv, c.kv_head0, c.n_kv, vpr);
+      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)v, (uint4*)Vc, S,
+                         pr.Hkv, c.kv_head0, c.n_kv, vpr);
+    }
+    const size_t nq = (size_t)S * pr.hc * vpr;
+    hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)q, (uint4*)Qc, S,
+                       pr.Hq, c.q_head0, pr.hc, vpr);
+    FwdParams<T> fp;
+    fp.q = Qc;
+    fp.k = Kc;
+    fp.v = Vc;
+    fp.o = Oc;
+    fp.lse = lse + (size_t)c.q_head0 * S;
+    fp.S = S;
+    fp.hc = pr.hc;
+    fp.heads_per_kv = pr.heads_per_kv;
+    fp.n_qtiles = n_qtiles;
+    fp.causal = pr.causal;
+    fp.scale_log2 = scale * kLog2e;
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, fp);
+    hipLaunchKernelGGL(unpack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)Oc, (uint4*)out, S,
+                       pr.Hq, c.q_head0, pr.hc, vpr);
+    if (int rc = check_launch("forward chunk")) return rc;
+  }
+  return UPIPE_OK;
+}
+
+template <typename T, int D>
+int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, const void* out, const void* dout,
+            const float* lse, void* dq, void* dk, void* dv, char* ws, hipStream_t st) {
+  const BwdPool pool = bwd_pool(pr);
+  const int S = (int)pr.S;
+  const int vpr = D * (int)sizeof(T) / 16;
+  T* Qc = reinterpret_cast<T*>(ws + pool.q);
+  T* dOc = reinterpret_cast<T*>(ws + pool.dout);
+  T* dQc = reinterpret_cast<T*>(ws + pool.dq);
+  T* Kc = reinterpret_cast<T*>(ws + pool.k);
+  T* Vc = reinterpret_cast<T*>(ws + pool.v);
+  float* Dc = reinterpret_cast<float*>(ws + pool.drow);
+  float* dKa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dk_acc) : nullptr;
+  float* dVa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dv_acc) : nullptr;
+  const int n_qtiles = (S + DqShape<T, D>::BQ - 1) / DqShape<T, D>::BQ;
+  const int n_ktiles = (S + DkvShape<T, D>::BKV - 1) / DkvShape<T, D>::BKV;
+  const float scale = 1.0f / std::sqrt((float)D);
+  constexpr int kRowsPerPreBlock = 256 / (D * (int)sizeof(T) / 16);
+  for (const Chunk& c : plan(pr)) {
+    if (c.load_kv) {
+      const size_t nv = (size_t)S * c.n_kv * vpr;
+      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)k, (uint4*)Kc, S,
+                         pr.Hkv, c.kv_head0, c.n_kv, vpr);
+      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)v, (uint4*)Vc, S,
+                         pr.Hkv, c.kv_head0, c.n_kv, vpr);
+    }
+    const size_t nq = (size_t)S * pr.hc * vpr;
+    hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)q, (uint4*)Qc, S,
+                       pr.Hq, c.q_head0, pr.hc, vpr);
+    const size_t rows = (size_t)S * pr.hc;
+    const unsigned pre_grid =
+        (unsigned)std::min<size_t>((rows + kRowsPerPreBlock - 1) / kRowsPerPreBlock, 256 * 32);
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st, (const T*)out, (const T*)dout, dOc, Dc,
+                       S, pr.Hq, c.q_head0, pr.hc);
+
+    BwdParams<T> bp;
+    bp.q = Qc;
+    bp.k = Kc;
+    bp.v = Vc;
+    bp.dout = dOc;
+    bp.lse = lse + (size_t)c.q_head0 * S;
+    bp.Drow = Dc;
+    bp.dq = dQc;
+    bp.dk_acc = dKa;
+    bp.dv_acc = dVa;
+    bp.dk_out = reinterpret_cast<T*>(dk) + (size_t)c.kv_head0 * D;
+    bp.dv_out = reinterpret_cast<T*>(dv) + (size_t)c.kv_head0 * D;
+    bp.Hkv_total = pr.Hkv;
+    bp.S = S;
+    bp.hc = pr.hc;
+    bp.heads_per_kv = pr.heads_per_kv;
+    bp.nkv = pr.nkv;
+    bp.n_qtiles = n_qtiles;
+    bp.n_ktiles = n_ktiles;
+    bp.causal = pr.causal;
+    bp.acc_load = !c.first_for_kv;
+    bp.finalize = c.last_for_kv;
+    bp.scale = scale;
+    bp.scale_log2 = scale * kLog2e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(n_ktiles * pr.nkv), dim3(256), 0, st, bp);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, bp);
+    hipLaunchKernelGGL(unpack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)dQc, (uint4*)dq, S,
+                       pr.Hq, c.q_head0, pr.hc, vpr);
+    if (int rc = check_launch("backward chunk")) return rc;
+  }
+  return UPIPE_OK;
+}
+
+}  // namespace
+}  // namespace upipe
+
+using namespace upipe;
+
+extern "C" {
+
+size_t upipe_attn_fwd_workspace_bytes(int64_t S, int Hq, int Hkv, int d, int head_chunk, int dtype) {
+  Problem pr;
+  if (validate(S, Hq, Hkv, d, head_chunk, 1, dtype, &pr) != UPIPE_OK) return 0;
+  g_error.clear();
+  return fwd_pool(pr).total;
+}
+
+size_t upipe_attn_bwd_workspace_bytes(int64_t S, int Hq, int Hkv, int d, int head_chunk, int dtype) {
+  Problem pr;
+  if (validate(S, Hq, Hkv, d, head_chunk, 1, dtype, &pr) != UPIPE_OK) return 0;
+  g_error.clear();
+  return bwd_pool(pr).total;
+}
+
+int upipe_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t S, int Hq, int Hkv,
+                   int d, int head_chunk, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  Problem pr;
+  if (int rc = validate(S, Hq, Hkv, d, head_chunk, causal, dtype, &pr)) return rc;
+  const void* ptrs[] = {q, k, v, out, lse, workspace};
+  const char* names[] = {"q", "k", "v", "out", "lse", "workspace"};
+  for (int i = 0; i < 6; ++i) {
+    if (!ptrs[i]) return fail(UPIPE_EINVAL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  const size_t need = fwd_pool(pr).total;
+  if (workspace_bytes < need)
+    return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  g_error.clear();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == UPIPE_BF16) {
+    if (d == 128) return run_fwd<bf16, 128>(pr, q, k, v, out, lse, ws, st);
+    return run_fwd<bf16, 64>(pr, q, k, v, out, lse, ws, st);
+  }
+  if (d == 128) return run_fwd<float, 128>(pr, q, k, v, out, lse, ws, st);
+  return run_fwd<float, 64>(pr, q, k, v, out, lse, ws, st);
+}
+
+int upipe_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int64_t S, int Hq, int Hkv, int d, int head_chunk, int causal,
+                   int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  Problem pr;
+  if (int rc = validate(S, Hq, Hkv, d, head_chunk, causal, dtype, &pr)) return rc;
+  const void* ptrs[] = {q, k, v, out, dout, lse, dq, dk, dv, workspace};
+  const char* names[] = {"q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "workspace"};
+  for (int i = 0; i < 10; ++i) {
+    if (!ptrs[i]) return fail(UPIPE_EINVAL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  const size_t need = bwd_pool(pr).total;
+  if (workspace_bytes < need)
+    return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  g_error.clear();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (dtype == UPIPE_BF16) {
+    if (d == 128) return run_bwd<bf16, 128>(pr, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+    return run_bwd<bf16, 64>(pr, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+  }
+  if (d == 128) return run_bwd<float, 128>(pr, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+  return run_bwd<float, 64>(pr, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+}
+
+int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks, int32_t* q_head0, int32_t* kv_head0,
+                    int32_t* n_kv, int32_t* flags) {
+  Problem pr;
+  if (int rc = validate(1, Hq, Hkv, 64, head_chunk, 1, UPIPE_BF16, &pr)) return rc;
+  const std::vector<Chunk> cs = plan(pr);
+  if (max_chunks < (int)cs.size())
+    return fail(UPIPE_EINVAL, "max_chunks (%d) smaller than the chunk count (%d)", max_chunks, (int)cs.size());
+  for (size_t i = 0; i < cs.size(); ++i) {
+    if (q_head0) q_head0[i] = cs[i].q_head0;
+    if (kv_head0) kv_head0[i] = cs[i].kv_head0;
+    if (n_kv) n_kv[i] = cs[i].n_kv;
+    if (flags) flags[i] = (cs[i].load_kv ? 1 : 0) | (cs[i].first_for_kv ? 2 : 0) | (cs[i].last_for_kv ? 4 : 0);
+  }
+  g_error.clear();
+  return (int)cs.size();
+}
+
+const char* upipe_last_error(void) { return g_error.c_str(); }
+
+}  // extern "C"

@@ -171,15 +171,16 @@ def _row_batches(rows: np.ndarray, S: int, causal: bool):
         start = end
 
 
-def forward_rows(q, k, v, rows, causal: bool = True):
+def forward_rows(q_rows, k, v, rows, causal: bool = True):
     """Exact O and LSE at selected query rows, O(S*d) work per row.
 
+    ``q_rows`` [R,Hq,d] holds the query vectors of positions ``rows``.
     Returns (out_rows [R,Hq,d], lse_rows [Hq,R]) in float64, in ``rows`` order.
     """
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
     rows = np.asarray(rows, dtype=np.int64)
-    S, Hq, d = q.shape
-    Hkv = k.shape[1]
+    S, Hkv, d = k.shape
+    Hq = q_rows.shape[1]
     tau = 1.0 / math.sqrt(d)
     out = np.zeros((len(rows), Hq, d))
     lse = np.zeros((Hq, len(rows)))
@@ -189,7 +190,7 @@ def forward_rows(q, k, v, rows, causal: bool = True):
         mask = _look_back_mask(r, n_cols, causal)
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
-            s = tau * (q[r, h, :] @ k[:n_cols, g, :].T)
+            s = tau * (q_rows[sel, h, :] @ k[:n_cols, g, :].T)
             if mask is not None:
                 s[mask] = -np.inf
             p, lse_blk = _softmax_rows(s)
@@ -198,16 +199,17 @@ def forward_rows(q, k, v, rows, causal: bool = True):
     return out, lse
 
 
-def backward_rows_dq(q, k, v, dout, rows, causal: bool = True):
+def backward_rows_dq(q_rows, k, v, dout_rows, rows, causal: bool = True):
     """Exact dQ at selected query rows, O(S*d) work per row.
 
+    ``q_rows`` and ``dout_rows`` [R,Hq,d] hold q and dO at positions ``rows``.
     D_hi needs only row i's own O, so each row is self-contained.
     Returns dq_rows [R,Hq,d] in float64, in ``rows`` order.
     """
-    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    q_rows, k, v, dout_rows = _f64(q_rows), _f64(k), _f64(v), _f64(dout_rows)
     rows = np.asarray(rows, dtype=np.int64)
-    S, Hq, d = q.shape
-    Hkv = k.shape[1]
+    S, Hkv, d = k.shape
+    Hq = q_rows.shape[1]
     tau = 1.0 / math.sqrt(d)
     dq = np.zeros((len(rows), Hq, d))
     for sel in _row_batches(rows, S, causal):
@@ -216,13 +218,13 @@ def backward_rows_dq(q, k, v, dout, rows, causal: bool = True):
         mask = _look_back_mask(r, n_cols, causal)
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
-            s = tau * (q[r, h, :] @ k[:n_cols, g, :].T)
+            s = tau * (q_rows[sel, h, :] @ k[:n_cols, g, :].T)
             if mask is not None:
                 s[mask] = -np.inf
             p, _ = _softmax_rows(s)
             o = p @ v[:n_cols, g, :]
-            D = (dout[r, h, :] * o).sum(axis=1)
-            dp = dout[r, h, :] @ v[:n_cols, g, :].T
+            D = (dout_rows[sel, h, :] * o).sum(axis=1)
+            dp = dout_rows[sel, h, :] @ v[:n_cols, g, :].T
             ds = p * (dp - D[:, None])
             dq[sel, h, :] = tau * (ds @ k[:n_cols, g, :])
     return dq
@@ -236,14 +238,15 @@ def backward_cols_dkdv(q, k, v, dout, cols, causal: bool = True):
     the cost is O(|rows| * S * d), which is small when the keys lie near the
     end of a causal sequence. Returns (dk_cols [C,Hkv,d], dv_cols [C,Hkv,d]).
     """
-    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    k, v = _f64(k), _f64(v)
     cols = np.asarray(cols, dtype=np.int64)
-    S, Hq, d = q.shape
-    Hkv = k.shape[1]
+    S, Hkv, d = k.shape
+    Hq = q.shape[1]
     tau = 1.0 / math.sqrt(d)
     first = int(cols.min()) if causal else 0
     need = np.arange(first, S)
-    o_need, lse_need = forward_rows(q, k, v, need, causal)
+    q_need, do_need = _f64(q[first:]), _f64(dout[first:])
+    o_need, lse_need = forward_rows(q_need, k, v, need, causal)
     dk = np.zeros((len(cols), Hkv, d))
     dv = np.zeros((len(cols), Hkv, d))
     n_rows = len(need)
@@ -254,8 +257,8 @@ def backward_cols_dkdv(q, k, v, dout, cols, causal: bool = True):
         excluded = (need[None, :] < cj[:, None]) if causal else None
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
-            qh = q[need, h, :]
-            doh = dout[need, h, :]
+            qh = q_need[:, h, :]
+            doh = do_need[:, h, :]
             s = tau * (k[cj, g, :] @ qh.T)  # [C, n_rows] = s_ij transposed
             p = np.exp(s - lse_need[h][None, :])
             if excluded is not None:

@@ -1,0 +1,143 @@
+"""C ABI checks that need no GPU: the library loads and exports every
+declared symbol, the head-chunk planner, pool sizes, and argument validation
+(which runs on the host before anything is enqueued)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_attention_upipe_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "upipe_attn.h")
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(upipe_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.lib()
+    names = declared_functions()
+    assert {"upipe_attn_fwd", "upipe_attn_bwd", "upipe_attn_fwd_workspace_bytes",
+            "upipe_attn_bwd_workspace_bytes", "upipe_attn_plan", "upipe_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+
+
+@pytest.mark.parametrize("Hq,Hkv,hc", [(4, 1, 1), (4, 1, 2), (4, 1, 4), (8, 1, 8), (8, 2, 1), (8, 2, 2),
+                                       (8, 2, 4), (8, 2, 8), (4, 4, 1), (4, 4, 4), (6, 2, 3)])
+def test_plan_covers_heads_in_order(Hq, Hkv, hc):
+    plan = L.upipe_attn_plan(Hq, Hkv, hc)
+    G = Hq // Hkv
+    assert len(plan) == Hq // hc
+    assert [c["q_head0"] for c in plan] == list(range(0, Hq, hc))
+    seen_first, seen_last = set(), set()
+    prev_kv = None
+    for c in plan:
+        heads = range(c["q_head0"], c["q_head0"] + hc)
+        kvs = sorted({h // G for h in heads})
+        assert c["kv_head0"] == kvs[0] and c["n_kv"] == len(kvs)
+        assert c["load_kv"] == (c["kv_head0"] != prev_kv)
+        prev_kv = c["kv_head0"]
+        if c["first_for_kv"]:
+            assert c["q_head0"] % G == 0
+            seen_first.add(c["kv_head0"])
+        if c["last_for_kv"]:
+            assert (c["q_head0"] + hc) % G == 0
+            seen_last.add(c["kv_head0"])
+    assert seen_first == seen_last == set(range(0, Hkv, max(1, hc // G)))
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,hcs", [(131072, 4, 1, 128, (1, 2, 4)), (5242880, 8, 1, 128, (1, 2, 4, 8)),
+                                            (1024, 4, 4, 64, (1, 4)), (1000, 8, 2, 128, (1, 2, 4, 8))])
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_pool_grows_strictly_with_head_chunk(S, Hq, Hkv, d, hcs, dtype):
+    fwd = [L.upipe_attn_fwd_workspace_bytes(S, Hq, Hkv, d, hc, dtype) for hc in hcs]
+    bwd = [L.upipe_attn_bwd_workspace_bytes(S, Hq, Hkv, d, hc, dtype) for hc in hcs]
+    assert all(a < b for a, b in zip(fwd, fwd[1:])), fwd
+    assert all(a < b for a, b in zip(bwd, bwd[1:])), bwd
+    es = 2 if dtype == 0 else 4
+    U = S * d * es
+    # the forward pool holds the chunk's q and out rows and its kv heads
+    for hc, n in zip(hcs, fwd):
+        nkv = max(1, hc // (Hq // Hkv))
+        assert 2 * hc * U + 2 * nkv * U <= n < 2 * hc * U + 2 * nkv * U + 4096
+
+
+def test_pool_at_5m_tokens_matches_plan():
+    # the largest share: S = 5,242,880, Hq = 8, Hkv = 1, d = 128, bf16
+    gib = 1 << 30
+    sizes = [L.upipe_attn_bwd_workspace_bytes(5242880, 8, 1, 128, hc, 0) / gib for hc in (1, 2, 4, 8)]
+    U = 5242880 * 128 * 2 / gib
+    expect = [3 * hc * U + 2 * U + hc * 5242880 * 4 / gib + (4 * U if hc < 8 else 0) for hc in (1, 2, 4, 8)]
+    for got, exp in zip(sizes, expect):
+        assert abs(got - exp) < 1e-3
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, S=256, Hq=4, Hkv=1, d=128, hc=1, causal=1, dtype=0,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return L.lib().upipe_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["S"], a["Hq"], a["Hkv"], a["d"],
+                                  a["hc"], a["causal"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _bwd(**kw):
+    a = dict(S=256, Hq=4, Hkv=1, d=128, hc=1, causal=1, dtype=0, ws_bytes=1 << 40, dq=FAKE)
+    a.update(kw)
+    return L.lib().upipe_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["dq"], FAKE, FAKE, a["S"], a["Hq"], a["Hkv"],
+                                  a["d"], a["hc"], a["causal"], a["dtype"], FAKE, a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(S=0), -1, "S must be"),
+    (dict(Hq=4, Hkv=3), -1, "multiple of Hkv"),
+    (dict(hc=3), -1, "must divide Hq"),
+    (dict(Hq=12, Hkv=2, hc=4), -1, "divide or be a multiple"),
+    (dict(causal=2), -1, "causal"),
+    (dict(d=96), -2, "head dim"),
+    (dict(dtype=7), -2, "dtype"),
+    (dict(S=1 << 25), -2, "2^31"),
+    (dict(q=None), -1, "q is NULL"),
+    (dict(lse=None), -1, "lse is NULL"),
+    (dict(out=ctypes.c_void_p(0x10008)), -1, "not 16-byte aligned"),
+    (dict(ws_bytes=1024), -3, "workspace too small"),
+])
+def test_forward_rejects_bad_arguments(kw, status, msg):
+    assert _fwd(**kw) == status
+    assert msg in L.upipe_last_error()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(hc=8), -1, "must divide Hq"),
+    (dict(dq=None), -1, "dq is NULL"),
+    (dict(ws_bytes=0), -3, "workspace too small"),
+    (dict(d=32), -2, "head dim"),
+])
+def test_backward_rejects_bad_arguments(kw, status, msg):
+    assert _bwd(**kw) == status
+    assert msg in L.upipe_last_error()
+
+
+def test_workspace_bytes_reports_errors():
+    assert L.lib().upipe_attn_fwd_workspace_bytes(0, 4, 1, 128, 1, 0) == 0
+    assert "S must be" in L.upipe_last_error()
+    with pytest.raises(L.UpipeError):
+        L.upipe_attn_bwd_workspace_bytes(16, 4, 1, 128, 3, 0)
+    assert L.upipe_attn_fwd_workspace_bytes(16, 4, 1, 128, 2, 0) > 0
+    assert L.upipe_last_error() == ""
+
+
+def test_plan_rejects_small_table():
+    n = 4
+    arrs = [(ctypes.c_int32 * 1)() for _ in range(4)]
+    assert L.lib().upipe_attn_plan(n, 1, 1, 1, *arrs) == -1
+    assert "max_chunks" in L.upipe_last_error()

@@ -1,0 +1,134 @@
+"""HIP path vs the fp64 CPU oracle, element by element, through the C ABI.
+
+Small sizes: full tensors (several 128-row tiles plus a ragged tail). Every
+case prints its shape before it runs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_close, bit_equal, f64, run
+from long_context_attention_upipe_amd.workloads import WORKLOADS, custom, make_inputs
+from oracle.attention import attention_backward, attention_forward
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _full_case(w, hcs, causal=True, check_bwd=True, rel_only=False):
+    dev = _dev()
+    print(f"\n  case {w.name} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} {w.dtype} causal={causal} hcs={hcs}", flush=True)
+    q, k, v, do = make_inputs(w, device="cpu")
+    ro, rl = attention_forward(f64(q), f64(k), f64(v), causal=causal)
+    if check_bwd:
+        rdq, rdk, rdv = attention_backward(f64(q), f64(k), f64(v), f64(do), causal=causal)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    first = None
+    for hc in hcs:
+        print(f"   head_chunk={hc}", flush=True)
+        r = run(qd, kd, vd, dod if check_bwd else None, hc, causal=causal)
+        assert_close("out", f64(r["out"]), ro, w.dtype)
+        assert_close("lse", f64(r["lse"]), rl, w.dtype)
+        if check_bwd:
+            assert_close("dq", f64(r["dq"]), rdq, w.dtype, rel_only)
+            assert_close("dk", f64(r["dk"]), rdk, w.dtype, rel_only)
+            assert_close("dv", f64(r["dv"]), rdv, w.dtype, rel_only)
+        if first is None:
+            first = r
+        else:
+            for name in r:
+                assert bit_equal(r[name], first[name]), f"{name} differs between head_chunk {hcs[0]} and {hc}"
+
+
+def test_mha_s1024_fp32_full_tensor():
+    """S=1024, Hq=Hkv=4, d=64, fp32, head_chunk 1 and 4; full tensors at 1e-4."""
+    _full_case(WORKLOADS["mha_s1k_fp32"], (1, 4))
+
+
+@pytest.mark.parametrize("S", [1, 2, 31, 64, 127, 128, 129, 300, 1000])
+def test_gqa_bf16_ragged_lengths(S):
+    _full_case(custom(S, 4, 1, 128, "bf16", seed=100 + S, dout_scaled=True), (1, 2, 4))
+
+
+def test_gqa_bf16_several_tiles_and_tail():
+    _full_case(custom(2309, 4, 1, 128, "bf16", seed=5, dout_scaled=True), (1, 2, 4))
+
+
+def test_gqa_two_kv_heads_every_chunk_size():
+    """Hkv=2: head_chunk 1 and 2 split a kv group over chunks (fp32 dK/dV
+    carried across chunks); 4 and 8 hold whole groups."""
+    _full_case(custom(700, 8, 2, 128, "bf16", seed=21, dout_scaled=True), (1, 2, 4, 8))
+
+
+def test_unscaled_dout_relative_error():
+    """dO ~ N(0,1) without the 1/sqrt(S) loss scaling: gradients reach |x| ~ 8,
+    where one bf16 rounding step alone is 1/32, so only the relative
+    Frobenius bound applies."""
+    _full_case(custom(1000, 4, 1, 128, "bf16", seed=99, dout_scaled=False), (4,), rel_only=True)
+
+
+def test_non_causal_bf16():
+    _full_case(custom(613, 4, 1, 128, "bf16", seed=31, dout_scaled=True), (1, 4), causal=False)
+
+
+def test_head_dim_64_bf16():
+    _full_case(custom(555, 4, 2, 64, "bf16", seed=41, dout_scaled=True), (1, 2, 4))
+
+
+def test_fp32_head_dim_128():
+    _full_case(custom(390, 2, 1, 128, "fp32", seed=51), (1, 2))
+
+
+def test_non_causal_fp32_mha():
+    _full_case(custom(257, 2, 2, 64, "fp32", seed=61), (1, 2), causal=False)
+
+
+def test_row0_is_v0_bit_exact_and_runs_repeat_bit_identical():
+    """Causal row 0 sees only key 0: out[0] = v[0] exactly in bf16. Two runs
+    of the same call give bit-identical outputs."""
+    dev = _dev()
+    w = custom(4099, 4, 1, 128, "bf16", seed=71)
+    q, k, v, do = (t.to(dev) for t in make_inputs(w, device="cpu"))
+    a = run(q, k, v, do, 2)
+    b = run(q, k, v, do, 2)
+    for name in a:
+        assert bit_equal(a[name], b[name]), f"{name} not deterministic"
+    for h in range(w.Hq):
+        assert torch.equal(a["out"][0, h], v[0, 0]), f"out[0,{h}] != v[0]"
+    lse0 = (q[0].float() @ k[0, 0].float()) / np.sqrt(w.d)
+    torch.testing.assert_close(a["lse"][:, 0], lse0, rtol=1e-5, atol=1e-5)
+
+
+def test_uniform_keys_closed_form():
+    """All keys equal: out_i is the mean of v_0..v_i, lse_i = <q_i,c>/sqrt(d) + ln(i+1)."""
+    dev = _dev()
+    w = custom(1500, 4, 1, 128, "bf16", seed=81)
+    q, k, v, do = make_inputs(w, device="cpu")
+    k[:] = k[0:1]
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    r = run(qd, kd, vd, None, 4)
+    vv = f64(v)[:, 0, :]
+    means = np.cumsum(vv, axis=0) / np.arange(1, w.S + 1)[:, None]
+    for h in range(w.Hq):
+        assert_close("out", f64(r["out"])[:, h, :], means, "bf16")
+        ref = f64(q)[:, h, :] @ f64(k)[0, 0] / np.sqrt(w.d) + np.log(np.arange(1, w.S + 1))
+        assert_close("lse", f64(r["lse"])[h], ref, "bf16")
+
+
+def test_gradient_column_sums():
+    """sum_j dK_j = 0 and sum_j dV_j = sum of dO over the group, at any size."""
+    dev = _dev()
+    w = custom(3000, 4, 1, 128, "bf16", seed=91, dout_scaled=True)
+    q, k, v, do = (t.to(dev) for t in make_inputs(w, device="cpu"))
+    r = run(q, k, v, do, 4)
+    dk_sum = f64(r["dk"]).sum(axis=0)[0]
+    dv_sum = f64(r["dv"]).sum(axis=0)[0]
+    scale = np.abs(f64(r["dk"])).sum(axis=0)[0]
+    assert np.all(np.abs(dk_sum) <= 2e-2 * scale + 1e-3), np.abs(dk_sum / scale).max()
+    assert_close("dvsum", dv_sum, f64(do).sum(axis=(0, 1)), "bf16")

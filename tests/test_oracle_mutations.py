@@ -24,8 +24,8 @@ MUTATIONS = {
     "rows_dq_missing_D": ("ds = p * (dp - D[:, None])\n            dq[sel", "ds = p * dp\n            dq[sel"),
     "cols_wrong_causal_side": ("(need[None, :] < cj[:, None])", "(need[None, :] > cj[:, None])"),
     "cols_dv_missing": ("dv[c0:c0 + per, g, :] += p @ doh", "dv[c0:c0 + per, g, :] += 0 * (p @ doh)"),
-    "fwd_rows_noncausal_width": ("n_cols = int(r.max()) + 1 if causal else S\n        mask = _look_back_mask(r, n_cols, causal)\n        for h in range(Hq):\n            g = kv_head_of(h, Hq, Hkv)\n            s = tau * (q[r, h, :] @ k[:n_cols, g, :].T)\n            if mask is not None:\n                s[mask] = -np.inf\n            p, lse_blk",
-                                 "n_cols = int(r.max()) + 1\n        mask = _look_back_mask(r, n_cols, causal)\n        for h in range(Hq):\n            g = kv_head_of(h, Hq, Hkv)\n            s = tau * (q[r, h, :] @ k[:n_cols, g, :].T)\n            if mask is not None:\n                s[mask] = -np.inf\n            p, lse_blk"),
+    "fwd_rows_noncausal_width": ("n_cols = int(r.max()) + 1 if causal else S\n        mask = _look_back_mask(r, n_cols, causal)\n        for h in range(Hq):\n            g = kv_head_of(h, Hq, Hkv)\n            s = tau * (q_rows[sel, h, :] @ k[:n_cols, g, :].T)\n            if mask is not None:\n                s[mask] = -np.inf\n            p, lse_blk",
+                                 "n_cols = int(r.max()) + 1\n        mask = _look_back_mask(r, n_cols, causal)\n        for h in range(Hq):\n            g = kv_head_of(h, Hq, Hkv)\n            s = tau * (q_rows[sel, h, :] @ k[:n_cols, g, :].T)\n            if mask is not None:\n                s[mask] = -np.inf\n            p, lse_blk"),
 }
 
 
