@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark: causal GQA attention forward+backward, UPipe head chunks, one GPU.
+
+One step = upipe_attn_fwd + upipe_attn_bwd over the whole workload: the
+chunk planner, the pack copies (the stand-in for the Ulysses exchange), the
+forward kernel, the unpack, the D pre-pass, the dK/dV and dQ kernels and the
+final copies, every head chunk reusing one fixed pool. Inputs are resident in
+HBM before the timed region starts.
+
+Prints ONE JSON line. `value` is algorithmic attention TFLOP/s for fwd+bwd:
+F = 14 * d * Hq * S(S+1)/2 per step (fwd 4*d per unmasked (row, key) pair:
+Q K^T and P V; bwd 10*d: the Q K^T recompute, dP, dV, dK and dQ). Masked
+pairs, softmax work and any extra recompute are not counted.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--head-chunk HC] [--sweep] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s & % bf16 MFMA peak at 1M-5M tokens; peak HBM"
+# MI355X dense bf16 MFMA peak: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz.
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP32_MFMA_TFLOPS = 157.3
+GIB = float(1 << 30)
+
+# Algorithmic FLOPs per unmasked (row, key) pair and head, per kernel, in units
+# of d: fwd = Q K^T + P V; dK/dV kernel = Q K^T (recompute) + dP + dV + dK;
+# dQ kernel = dQ only (its Q K^T and dP recomputes duplicate the dK/dV kernel's).
+ALGO_FLOPS_PER_PAIR_D = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 2}
+EXEC_FLOPS_PER_PAIR_D = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 6}
+
+
+def pairs(S: int, causal: bool) -> int:
+    return S * (S + 1) // 2 if causal else S * S
+
+
+def cpu_baseline(w, q, k, v, do, s_prefix: int):
+    """Time the fp64 CPU oracle (as it stands) on the first s_prefix positions
+    of the same inputs: a causal fwd+bwd of that prefix, all heads."""
+    import numpy as np
+
+    from oracle.attention import attention_backward  # checker only: the CPU leg
+
+    try:
+        import threadpoolctl
+
+        threads = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    sl = slice(0, s_prefix)
+    arrs = [t[sl].float().cpu().numpy().astype(np.float64) for t in (q, k, v, do)]
+    t0 = time.perf_counter()
+    attention_backward(*arrs, causal=w.causal)  # recomputes the forward inside
+    dt = time.perf_counter() - t0
+    flops = 14 * w.d * w.Hq * pairs(s_prefix, w.causal)
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle, causal fwd+bwd of the first {s_prefix} positions of the same "
+                  f"inputs (Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}), {dt:.1f} s",
+        "seconds": round(dt, 3),
+    }
+
+
+def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
+    import torch
+
+    import long_context_attention_upipe_amd as up
+    from long_context_attention_upipe_amd.workloads import make_inputs
+
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    q, k, v, do = make_inputs(w, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.Hq, w.S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    code = up.dtype_code(q.dtype)
+    ws_bytes = max(up.upipe_attn_fwd_workspace_bytes(w.S, w.Hq, w.Hkv, w.d, head_chunk, code),
+                   up.upipe_attn_bwd_workspace_bytes(w.S, w.Hq, w.Hkv, w.d, head_chunk, code))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        up.upipe_attn_fwd(q, k, v, out, lse, head_chunk, w.causal, ws, stream)
+
+    def bwd():
+        up.upipe_attn_bwd(q, k, v, out, do, lse, dq, dk, dv, head_chunk, w.causal, ws, stream)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize(dev)
+    print(f"[bench] warmup done: {w.name} head_chunk={head_chunk}", file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    up.upipe_profile_reset()
+    up.upipe_profile_enable(True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    up.upipe_profile_enable(False)
+    prof = up.upipe_profile_read()
+    up.upipe_profile_reset()
+
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    ms_per_step = (t1 - t0) * 1000.0 / steps
+    P = pairs(w.S, w.causal)
+    f_fwd = 4 * w.d * w.Hq * P
+    f_bwd = 10 * w.d * w.Hq * P
+    peak_alloc = torch.cuda.max_memory_allocated(dev) - base
+    kernels = {}
+    for name, (launches, total_ms) in prof.items():
+        avg = total_ms / max(1, launches)
+        entry = {"launches": launches, "avg_ms": round(avg, 4), "total_ms_per_step": round(total_ms / steps, 3)}
+        if name in ALGO_FLOPS_PER_PAIR_D:
+            per_launch = ALGO_FLOPS_PER_PAIR_D[name] * w.d * head_chunk * P
+            execd = EXEC_FLOPS_PER_PAIR_D[name] * w.d * head_chunk * P
+            entry["algo_tflops"] = round(per_launch / (avg / 1e3) / 1e12, 2)
+            entry["exec_tflops"] = round(execd / (avg / 1e3) / 1e12, 2)
+        kernels[name] = entry
+    res = {
+        "head_chunk": head_chunk,
+        "ms_per_step": ms_per_step,
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "tflops": (f_fwd + f_bwd) / (ms_per_step / 1e3) / 1e12,
+        "fwd_tflops": f_fwd / (fwd_ms / 1e3) / 1e12,
+        "bwd_tflops": f_bwd / (bwd_ms / 1e3) / 1e12,
+        "peak_hbm_gib": peak_alloc / GIB,
+        "workspace_gib": ws_bytes / GIB,
+        "kernels": kernels,
+    }
+    tensors = (q, k, v, do)
+    del out, lse, dq, dk, dv, ws
+    return res, tensors
+
+
+def roofline(w, res, head_chunk):
+    """Roofline entry for the attention kernel with the most time per step."""
+    attn = {n: e for n, e in res["kernels"].items() if n in ALGO_FLOPS_PER_PAIR_D}
+    name = max(attn, key=lambda n: attn[n]["total_ms_per_step"])
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    achieved = attn[name]["algo_tflops"]
+    return {
+        "kernel": name,
+        "bound": "mfma",
+        "achieved": achieved,
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None,
+        "per_unit": f"{ALGO_FLOPS_PER_PAIR_D[name]}*d FLOP per unmasked (row, key) pair and head; "
+                    f"{head_chunk} heads x S(S+1)/2 pairs per launch",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama8b_share_s1m")
+    ap.add_argument("--head-chunk", type=int, default=None, help="default: the workload's smallest")
+    ap.add_argument("--sweep", action="store_true", help="also run every head_chunk of the workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-prefix", type=int, default=32768, help="positions in the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (3 launches), to scale HBM counters")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the path "
+              "has no collectives; per-GPU shares are independent under head sharding.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from long_context_attention_upipe_amd.workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (no CPU fallback)", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 3}), flush=True)
+        return
+    w = WORKLOADS[args.workload]
+    hc = args.head_chunk or min(w.head_chunks)
+    props = torch.cuda.get_device_properties(dev)
+    print(f"[bench] {props.name} CUs={props.multi_processor_count} workload={w.name} S={w.S} "
+          f"Hq={w.Hq} Hkv={w.Hkv} d={w.d} {w.dtype} head_chunk={hc}", file=sys.stderr, flush=True)
+
+    res, tensors = run_one(w, hc, args.steps, args.warmup, dev)
+    print(f"[bench] timed: {res['ms_per_step']:.1f} ms/step, {res['tflops']:.1f} TFLOP/s", file=sys.stderr,
+          flush=True)
+    sweep = []
+    if args.sweep:
+        for h in w.head_chunks:
+            r = res if h == hc else run_one(w, h, args.steps, args.warmup, dev)[0]
+            sweep.append({k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items()
+                          if k_ != "kernels"})
+            print(f"[bench] sweep head_chunk={h}: {r['tflops']:.1f} TFLOP/s peak {r['peak_hbm_gib']:.2f} GiB",
+                  file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        q, k, v, do = tensors
+        cpu = cpu_baseline(w, q, k, v, do, min(args.cpu_prefix, w.S))
+        print(f"[bench] cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads", file=sys.stderr,
+              flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(res["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v, dO ~ N(0,1)/sqrt(S), drawn on device)",
+        "config": {"workload": w.name, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "head_chunk": hc,
+                   "causal": w.causal, "parallelism": "1 GPU's Ulysses head share, UPipe head chunks"},
+        "pct_bf16_peak": round(100.0 * res["tflops"] / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(res["fwd_ms"], 3),
+        "bwd_ms": round(res["bwd_ms"], 3),
+        "fwd_tflops": round(res["fwd_tflops"], 2),
+        "bwd_tflops": round(res["bwd_tflops"], 2),
+        "peak_hbm_gib": round(res["peak_hbm_gib"], 3),
+        "workspace_gib": round(res["workspace_gib"], 3),
+        "roofline": roofline(w, res, hc),
+        "cpu_baseline": cpu,
+        "kernels": res["kernels"],
+    }
+    if sweep:
+        line["head_chunk_sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

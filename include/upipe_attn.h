@@ -128,6 +128,19 @@ int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks,
                     int32_t* q_head0, int32_t* kv_head0, int32_t* n_kv,
                     int32_t* flags);
 
+/*
+ * Kernel timing for measurement. While enabled, every kernel the library
+ * enqueues is bracketed by a pair of HIP events recorded on the launch stream
+ * itself. upipe_profile_read() waits for the recorded events, adds their
+ * elapsed times into per-kernel totals, and copies up to max_kernels entries:
+ * names[i] (static strings), launches[i], total_ms[i]. Returns the number of
+ * kernel kinds seen since the last reset (host only; not thread-safe against
+ * concurrent launches). upipe_profile_reset() drops all totals and events.
+ */
+int upipe_profile_enable(int on);
+int upipe_profile_read(int max_kernels, const char** names, int64_t* launches, double* total_ms);
+void upipe_profile_reset(void);
+
 /* Message for the last failed call on this thread ("" if none). Valid until
  * the next call into the library on the same thread. */
 const char* upipe_last_error(void);

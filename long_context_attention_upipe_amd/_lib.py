@@ -52,6 +52,13 @@ def lib() -> ctypes.CDLL:
     p32 = ctypes.POINTER(ctypes.c_int32)
     L.upipe_attn_plan.argtypes = [i32, i32, i32, i32, p32, p32, p32, p32]
     L.upipe_attn_plan.restype = i32
+    L.upipe_profile_enable.argtypes = [i32]
+    L.upipe_profile_enable.restype = i32
+    L.upipe_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
+                                     ctypes.POINTER(ctypes.c_double)]
+    L.upipe_profile_read.restype = i32
+    L.upipe_profile_reset.argtypes = []
+    L.upipe_profile_reset.restype = None
     L.upipe_last_error.argtypes = []
     L.upipe_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -148,3 +155,24 @@ def upipe_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, head_chunk, causal, work
                                 _ptr(dq), _ptr(dk), _ptr(dv), S, Hq, Hkv, d,
                                 int(head_chunk), int(causal), dtype_code(q.dtype),
                                 _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+
+
+def upipe_profile_enable(on: bool) -> None:
+    """Bracket every library kernel launch with HIP events on its stream."""
+    lib().upipe_profile_enable(1 if on else 0)
+
+
+def upipe_profile_reset() -> None:
+    lib().upipe_profile_reset()
+
+
+def upipe_profile_read():
+    """{kernel name: (launches, total ms)} since the last reset (waits for the events)."""
+    n_max = 16
+    names = (ctypes.c_char_p * n_max)()
+    launches = (ctypes.c_int64 * n_max)()
+    ms = (ctypes.c_double * n_max)()
+    n = lib().upipe_profile_read(n_max, names, launches, ms)
+    if n < 0:
+        raise UpipeError(n, upipe_last_error())
+    return {names[i].decode(): (int(launches[i]), float(ms[i])) for i in range(min(n, n_max))}

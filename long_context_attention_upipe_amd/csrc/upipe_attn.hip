@@ -145,6 +145,71 @@ BwdPool bwd_pool(const Problem& pr) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// ---------------------------------------------------------------------------
+// Optional per-kernel timing with HIP events on the launch stream.
+// ---------------------------------------------------------------------------
+enum KernelId { K_PACK = 0, K_UNPACK, K_FWD, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"pack_heads", "unpack_heads", "attn_fwd", "bwd_pre", "attn_bwd_dkdv",
+                                           "attn_bwd_dq"};
+struct Profiler {
+  bool on = false;
+  struct Rec {
+    int id;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> pending;
+  int64_t launches[K_COUNT] = {};
+  double ms[K_COUNT] = {};
+};
+Profiler g_prof;
+
+// Launch `fn` on stream `st`, bracketed by events when profiling is on.
+template <typename Fn>
+void timed(int id, hipStream_t st, Fn&& fn) {
+  if (!g_prof.on) {
+    fn();
+    return;
+  }
+  Profiler::Rec r;
+  r.id = id;
+  if (hipEventCreate(&r.a) != hipSuccess) {
+    fn();
+    return;
+  }
+  if (hipEventCreate(&r.b) != hipSuccess) {
+    (void)hipEventDestroy(r.a);
+    fn();
+    return;
+  }
+  const bool ok_a = hipEventRecord(r.a, st) == hipSuccess;
+  fn();
+  const bool ok_b = hipEventRecord(r.b, st) == hipSuccess;
+  if (ok_a && ok_b) {
+    g_prof.pending.push_back(r);
+  } else {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+}
+
+int profile_flush() {
+  for (Profiler::Rec& r : g_prof.pending) {
+    hipError_t e = hipEventSynchronize(r.b);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+    if (e != hipSuccess) {
+      g_prof.pending.clear();
+      return fail(UPIPE_EHIP, "profile: %s", hipGetErrorString(e));
+    }
+    g_prof.launches[r.id] += 1;
+    g_prof.ms[r.id] += t;
+  }
+  g_prof.pending.clear();
+  return UPIPE_OK;
+}
+
 unsigned copy_grid(size_t vectors) {
   const size_t blocks = (vectors + 255) / 256;
   return (unsigned)std::min<size_t>(std::max<size_t>(blocks, 1), 256 * 32);
@@ -171,14 +236,20 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
   for (const Chunk& c : plan(pr)) {
     if (c.load_kv) {
       const size_t nv = (size_t)S * c.n_kv * vpr;
-      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)k, (uint4*)Kc, S,
-                         pr.Hkv, c.kv_head0, c.n_kv, vpr);
-      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)v, (uint4*)Vc, S,
-                         pr.Hkv, c.kv_head0, c.n_kv, vpr);
+      timed(K_PACK, st, [&] {
+        hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)k, (uint4*)Kc, S,
+                           pr.Hkv, c.kv_head0, c.n_kv, vpr);
+      });
+      timed(K_PACK, st, [&] {
+        hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)v, (uint4*)Vc, S,
+                           pr.Hkv, c.kv_head0, c.n_kv, vpr);
+      });
     }
     const size_t nq = (size_t)S * pr.hc * vpr;
-    hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)q, (uint4*)Qc, S,
-                       pr.Hq, c.q_head0, pr.hc, vpr);
+    timed(K_PACK, st, [&] {
+      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)q, (uint4*)Qc, S,
+                         pr.Hq, c.q_head0, pr.hc, vpr);
+    });
     FwdParams<T> fp;
     fp.q = Qc;
     fp.k = Kc;
@@ -191,9 +262,13 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     fp.n_qtiles = n_qtiles;
     fp.causal = pr.causal;
     fp.scale_log2 = scale * kLog2e;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, fp);
-    hipLaunchKernelGGL(unpack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)Oc, (uint4*)out, S,
-                       pr.Hq, c.q_head0, pr.hc, vpr);
+    timed(K_FWD, st, [&] {
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, fp);
+    });
+    timed(K_UNPACK, st, [&] {
+      hipLaunchKernelGGL(unpack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)Oc, (uint4*)out, S,
+                         pr.Hq, c.q_head0, pr.hc, vpr);
+    });
     if (int rc = check_launch("forward chunk")) return rc;
   }
   return UPIPE_OK;
@@ -220,19 +295,27 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
   for (const Chunk& c : plan(pr)) {
     if (c.load_kv) {
       const size_t nv = (size_t)S * c.n_kv * vpr;
-      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)k, (uint4*)Kc, S,
-                         pr.Hkv, c.kv_head0, c.n_kv, vpr);
-      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)v, (uint4*)Vc, S,
-                         pr.Hkv, c.kv_head0, c.n_kv, vpr);
+      timed(K_PACK, st, [&] {
+        hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)k, (uint4*)Kc, S,
+                           pr.Hkv, c.kv_head0, c.n_kv, vpr);
+      });
+      timed(K_PACK, st, [&] {
+        hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)v, (uint4*)Vc, S,
+                           pr.Hkv, c.kv_head0, c.n_kv, vpr);
+      });
     }
     const size_t nq = (size_t)S * pr.hc * vpr;
-    hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)q, (uint4*)Qc, S,
-                       pr.Hq, c.q_head0, pr.hc, vpr);
+    timed(K_PACK, st, [&] {
+      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)q, (uint4*)Qc, S,
+                         pr.Hq, c.q_head0, pr.hc, vpr);
+    });
     const size_t rows = (size_t)S * pr.hc;
     const unsigned pre_grid =
         (unsigned)std::min<size_t>((rows + kRowsPerPreBlock - 1) / kRowsPerPreBlock, 256 * 32);
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st, (const T*)out, (const T*)dout, dOc, Dc,
-                       S, pr.Hq, c.q_head0, pr.hc);
+    timed(K_BWD_PRE, st, [&] {
+      hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st, (const T*)out, (const T*)dout, dOc,
+                         Dc, S, pr.Hq, c.q_head0, pr.hc);
+    });
 
     BwdParams<T> bp;
     bp.q = Qc;
@@ -258,10 +341,16 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     bp.finalize = c.last_for_kv;
     bp.scale = scale;
     bp.scale_log2 = scale * kLog2e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(n_ktiles * pr.nkv), dim3(256), 0, st, bp);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, bp);
-    hipLaunchKernelGGL(unpack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)dQc, (uint4*)dq, S,
-                       pr.Hq, c.q_head0, pr.hc, vpr);
+    timed(K_BWD_DKDV, st, [&] {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(n_ktiles * pr.nkv), dim3(256), 0, st, bp);
+    });
+    timed(K_BWD_DQ, st, [&] {
+      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, bp);
+    });
+    timed(K_UNPACK, st, [&] {
+      hipLaunchKernelGGL(unpack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)dQc, (uint4*)dq, S,
+                         pr.Hq, c.q_head0, pr.hc, vpr);
+    });
     if (int rc = check_launch("backward chunk")) return rc;
   }
   return UPIPE_OK;
@@ -353,6 +442,38 @@ int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks, int32_t* q_
   }
   g_error.clear();
   return (int)cs.size();
+}
+
+int upipe_profile_enable(int on) {
+  g_prof.on = on != 0;
+  return UPIPE_OK;
+}
+
+int upipe_profile_read(int max_kernels, const char** names, int64_t* launches, double* total_ms) {
+  if (int rc = profile_flush()) return rc;
+  int n = 0;
+  for (int i = 0; i < K_COUNT; ++i) {
+    if (!g_prof.launches[i]) continue;
+    if (n < max_kernels) {
+      if (names) names[n] = kKernelNames[i];
+      if (launches) launches[n] = g_prof.launches[i];
+      if (total_ms) total_ms[n] = g_prof.ms[i];
+    }
+    ++n;
+  }
+  return n;
+}
+
+void upipe_profile_reset(void) {
+  for (Profiler::Rec& r : g_prof.pending) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.pending.clear();
+  for (int i = 0; i < K_COUNT; ++i) {
+    g_prof.launches[i] = 0;
+    g_prof.ms[i] = 0;
+  }
 }
 
 const char* upipe_last_error(void) { return g_error.c_str(); }
