@@ -1,0 +1,427 @@
+// bf16 attention kernels for gfx950: forward, dQ and dK/dV.
+//
+// Same mathematics, orientation and determinism contract as the generic
+// kernels (attn_fwd.hpp, attn_bwd.hpp), re-tiled for bf16 on CDNA4:
+//  * K/V (forward, dQ) and Q/dO (dK/dV) tiles go global -> LDS directly, into
+//    double-buffered XOR-swizzled row-major tiles (lds_tiles.hpp): one barrier
+//    per tile, no staging registers;
+//  * operands that contract over a tile's rows (V^T in P V, K^T in dS K,
+//    dO^T in dV, Q^T in dK) are read transposed from the same row-major tile
+//    with ds_read_b64_tr_b16 instead of keeping a second, transposed copy;
+//  * register budgets fit two waves per SIMD, so one wave's softmax VALU
+//    work overlaps the other wave's MFMAs.
+#pragma once
+
+#include "attn_bwd.hpp"
+#include "attn_fwd.hpp"
+#include "lds_tiles.hpp"
+
+namespace upipe {
+
+// ---------------------------------------------------------------------------
+// Forward: 4 waves x 32 query rows, 64-key tiles.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p) {
+  constexpr int BQ = 128, BK = 64, NKS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 sK[2][BK * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[2][BK * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int S = p.S;
+
+  const int t = blockIdx.x;
+  const int qt = p.causal ? (p.n_qtiles - 1 - t / p.hc) : (t / p.hc);
+  const int hl = t % p.hc;
+  const int kvl = hl / p.heads_per_kv;
+  const size_t head_elems = (size_t)S * D;
+  const bf16* __restrict__ Q = p.q + (size_t)hl * head_elems;
+  const bf16* __restrict__ K = p.k + (size_t)kvl * head_elems;
+  const bf16* __restrict__ V = p.v + (size_t)kvl * head_elems;
+
+  const int row0 = qt * BQ;
+  const int wrow0 = row0 + wave * 32;
+  const int my_row = wrow0 + col;
+
+  const int last_row = min(S, row0 + BQ) - 1;
+  const int n_kt = p.causal ? (last_row / BK + 1) : ((S + BK - 1) / BK);
+
+  tile_load_async<D, BK, 4>(sK[0], K, 0, S, wave, lane);
+  tile_load_async<D, BK, 4>(sV[0], V, 0, S, wave, lane);
+
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = my_row < S ? *reinterpret_cast<const bf16x8*>(Q + (size_t)my_row * D + ks * 16 + half * 8) : bf16x8{};
+
+  floatx16 o_acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o_acc[db] = floatx16{};
+  const float NEG_INF = -__builtin_inff();
+  float m_run = NEG_INF;
+  float l_run = 0.f;
+
+  wait_vm();
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < n_kt) {
+      tile_load_async<D, BK, 4>(sK[cur ^ 1], K, (kt + 1) * BK, S, wave, lane);
+      tile_load_async<D, BK, 4>(sV[cur ^ 1], V, (kt + 1) * BK, S, wave, lane);
+    }
+    const int key0 = kt * BK;
+    const bool active = (wrow0 < S) && (!p.causal || key0 <= wrow0 + 31);
+    if (active) {
+      floatx16 s[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        s[b] = floatx16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) mma32(s[b], tile_row_frag<D>(sK[cur], b * 32 + col, 2 * ks + half), qf[ks]);
+      }
+      const bool need_mask = (p.causal && key0 + BK - 1 > wrow0) || (key0 + BK > S);
+      if (need_mask) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = key0 + b * 32 + c_row(j, half);
+            if ((p.causal && key > my_row) || key >= S) s[b][j] = NEG_INF;
+          }
+      }
+      float mx = NEG_INF;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[b][j]);
+      mx = wave_xor32_max(mx);
+      const float m_new = fmaxf(m_run, mx * p.scale_log2);
+      const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      // Rescale only when some row's max moved (alpha == 1 otherwise: exact skip).
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o_acc[db] *= alpha;
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          s[b][j] = __builtin_amdgcn_exp2f(fmaf(s[b][j], p.scale_log2, -m_use));
+          psum += s[b][j];
+        }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          floatx8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = s[b][st * 8 + e];
+          const bf16x8 pf = to_frag(pv, bf16());
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            mma32(o_acc[db], tile_tr_frag<D>(sV[cur], b * 32 + st * 16, db * 32, lane), pf);
+        }
+    }
+    wait_vm();
+    __syncthreads();
+  }
+
+  const float l_tot = wave_xor32_sum(l_run);
+  if (my_row < S) {
+    const float inv = 1.f / l_tot;
+    bf16* O = p.o + (size_t)hl * head_elems + (size_t)my_row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        floatx4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = o_acc[db][jg * 4 + e] * inv;
+        *reinterpret_cast<bf16x4*>(O + db * 32 + jg * 8 + half * 4) = to_out4(o4, bf16());
+      }
+    if (half == 0) p.lse[(size_t)hl * S + my_row] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: 4 waves x 32 query rows, 64-key tiles, one 32-key block at a time.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16> p) {
+  constexpr int BQ = 128, BK = 64, NKS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 sK[2][BK * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[2][BK * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int S = p.S;
+
+  const int t = blockIdx.x;
+  const int qt = p.causal ? (p.n_qtiles - 1 - t / p.hc) : (t / p.hc);
+  const int hl = t % p.hc;
+  const int kvl = hl / p.heads_per_kv;
+  const size_t head_elems = (size_t)S * D;
+  const bf16* __restrict__ Q = p.q + (size_t)hl * head_elems;
+  const bf16* __restrict__ dO = p.dout + (size_t)hl * head_elems;
+  const bf16* __restrict__ K = p.k + (size_t)kvl * head_elems;
+  const bf16* __restrict__ V = p.v + (size_t)kvl * head_elems;
+
+  const int row0 = qt * BQ;
+  const int wrow0 = row0 + wave * 32;
+  const int my_row = wrow0 + col;
+  const bool row_ok = my_row < S;
+
+  const int last_row = min(S, row0 + BQ) - 1;
+  const int n_kt = p.causal ? (last_row / BK + 1) : ((S + BK - 1) / BK);
+
+  tile_load_async<D, BK, 4>(sK[0], K, 0, S, wave, lane);
+  tile_load_async<D, BK, 4>(sV[0], V, 0, S, wave, lane);
+
+  bf16x8 qf[NKS], df[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(Q + (size_t)my_row * D + ks * 16 + half * 8) : bf16x8{};
+    df[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(dO + (size_t)my_row * D + ks * 16 + half * 8) : bf16x8{};
+  }
+  const float l2 = row_ok ? p.lse2[(size_t)hl * S + my_row] : 0.f;
+  const float Dr = row_ok ? p.Drow[(size_t)hl * S + my_row] : 0.f;
+
+  floatx16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = floatx16{};
+
+  wait_vm();
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < n_kt) {
+      tile_load_async<D, BK, 4>(sK[cur ^ 1], K, (kt + 1) * BK, S, wave, lane);
+      tile_load_async<D, BK, 4>(sV[cur ^ 1], V, (kt + 1) * BK, S, wave, lane);
+    }
+    const int key0 = kt * BK;
+    const bool active = (wrow0 < S) && (!p.causal || key0 <= wrow0 + 31);
+    if (active) {
+      const bool need_mask = (p.causal && key0 + BK - 1 > wrow0) || (key0 + BK > S);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        floatx16 s = floatx16{}, dp = floatx16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          mma32(s, tile_row_frag<D>(sK[cur], b * 32 + col, 2 * ks + half), qf[ks]);
+          mma32(dp, tile_row_frag<D>(sV[cur], b * 32 + col, 2 * ks + half), df[ks]);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2));
+          if (need_mask) {
+            const int key = key0 + b * 32 + c_row(j, half);
+            if ((p.causal && key > my_row) || key >= S) pij = 0.f;
+          }
+          s[j] = pij * (dp[j] - Dr);  // dS^T
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          floatx8 d8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d8[e] = s[st * 8 + e];
+          const bf16x8 dsf = to_frag(d8, bf16());
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            mma32(acc[db], tile_tr_frag<D>(sK[cur], b * 32 + st * 16, db * 32, lane), dsf);
+        }
+      }
+    }
+    wait_vm();
+    __syncthreads();
+  }
+
+  if (row_ok) {
+    bf16* dQ = p.dq + (size_t)hl * head_elems + (size_t)my_row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        floatx4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[db][jg * 4 + e] * p.scale;
+        *reinterpret_cast<bf16x4*>(dQ + db * 32 + jg * 8 + half * 4) = to_out4(v4, bf16());
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV: 4 waves x 32 keys; query rows in steps of 32 (head-major, ascending).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf16> p) {
+  constexpr int BKV = 128, BQ = 32, NKS = D / 16, NDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) bf16 sQ[2][BQ * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sO[2][BQ * D];  // dO rows
+  __shared__ __attribute__((aligned(256))) float sLD[2][2 * BQ];  // lse*log2(e) | D
+  __shared__ __attribute__((aligned(1024))) bf16 sV[BKV * D];     // this workgroup's V rows
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int S = p.S;
+
+  const int t = blockIdx.x;
+  const int kt = t / p.nkv;
+  const int g = t % p.nkv;
+  const size_t head_elems = (size_t)S * D;
+  const bf16* __restrict__ K = p.k + (size_t)g * head_elems;
+  const bf16* __restrict__ V = p.v + (size_t)g * head_elems;
+
+  const int key0 = kt * BKV;
+  const int wkey0 = key0 + wave * 32;
+  const int my_key = wkey0 + col;
+  const bool key_ok = my_key < S;
+
+  const int n_qb = (S + BQ - 1) / BQ;
+  const int qb0 = p.causal ? key0 / BQ : 0;
+  const int steps_per_head = n_qb - qb0;
+  const int n_steps = p.heads_per_kv * steps_per_head;
+
+  auto issue = [&](int step, int buf) {
+    const int hi = step / steps_per_head;
+    const int qb = qb0 + step % steps_per_head;
+    const int hl = g * p.heads_per_kv + hi;
+    const int r0 = qb * BQ;
+    tile_load_async<D, BQ, 4>(sQ[buf], p.q + (size_t)hl * head_elems, r0, S, wave, lane);
+    tile_load_async<D, BQ, 4>(sO[buf], p.dout + (size_t)hl * head_elems, r0, S, wave, lane);
+    if (wave == 0) {
+      const int r = min(r0 + (lane & 31), S - 1);
+      const float* src = (lane < 32 ? p.lse2 : p.Drow) + (size_t)hl * S + r;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&sLD[buf][0], 4, 0, 0);
+    }
+  };
+
+  // V^T operand of dP = dO V^T stays in LDS (read per step); K^T stays in
+  // registers: both together would not fit two waves per SIMD.
+  tile_load_async<D, BKV, 4>(sV, V, key0, S, wave, lane);
+  issue(0, 0);
+
+  bf16x8 kf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    kf[ks] = key_ok ? *reinterpret_cast<const bf16x8*>(K + (size_t)my_key * D + ks * 16 + half * 8) : bf16x8{};
+
+  floatx16 dk[NDB], dv[NDB];
+  if (p.acc_load) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const size_t off = (size_t)g * head_elems + (size_t)my_key * D + db * 32 + jg * 8 + half * 4;
+        const floatx4 a = key_ok ? *reinterpret_cast<const floatx4*>(p.dk_acc + off) : floatx4{};
+        const floatx4 b = key_ok ? *reinterpret_cast<const floatx4*>(p.dv_acc + off) : floatx4{};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dk[db][jg * 4 + e] = a[e];
+          dv[db][jg * 4 + e] = b[e];
+        }
+      }
+  } else {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      dk[db] = floatx16{};
+      dv[db] = floatx16{};
+    }
+  }
+
+  wait_vm();
+  __syncthreads();
+  for (int step = 0; step < n_steps; ++step) {
+    const int cur = step & 1;
+    if (step + 1 < n_steps) issue(step + 1, cur ^ 1);
+    const int r0 = (qb0 + step % steps_per_head) * BQ;
+    const bool active = (wkey0 < S) && !(p.causal && r0 + BQ - 1 < wkey0);
+    if (active) {
+      floatx16 s = floatx16{}, dp = floatx16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        mma32(s, tile_row_frag<D>(sQ[cur], col, 2 * ks + half), kf[ks]);
+        mma32(dp, tile_row_frag<D>(sO[cur], col, 2 * ks + half), tile_row_frag<D>(sV, wave * 32 + col, 2 * ks + half));
+      }
+      const bool need_mask = (p.causal && r0 < wkey0 + 31) || (r0 + BQ > S);
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const floatx4 l4 = *reinterpret_cast<const floatx4*>(&sLD[cur][jg * 8 + half * 4]);
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(&sLD[cur][BQ + jg * 8 + half * 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = jg * 4 + e;
+          float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l4[e]));
+          if (need_mask) {
+            const int row = r0 + c_row(j, half);
+            if ((p.causal && my_key > row) || row >= S) pij = 0.f;
+          }
+          s[j] = pij;
+          dp[j] = pij * (dp[j] - d4[e]);
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        floatx8 p8, d8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p8[e] = s[st * 8 + e];
+          d8[e] = dp[st * 8 + e];
+        }
+        const bf16x8 pf = to_frag(p8, bf16());
+        const bf16x8 dsf = to_frag(d8, bf16());
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          mma32(dv[db], tile_tr_frag<D>(sO[cur], st * 16, db * 32, lane), pf);
+          mma32(dk[db], tile_tr_frag<D>(sQ[cur], st * 16, db * 32, lane), dsf);
+        }
+      }
+    }
+    wait_vm();
+    __syncthreads();
+  }
+
+  if (!key_ok) return;
+  if (p.finalize) {
+    bf16* dK = p.dk_out + ((size_t)my_key * p.Hkv_total + g) * D;
+    bf16* dV = p.dv_out + ((size_t)my_key * p.Hkv_total + g) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        floatx4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = dk[db][jg * 4 + e] * p.scale;
+          b[e] = dv[db][jg * 4 + e];
+        }
+        *reinterpret_cast<bf16x4*>(dK + db * 32 + jg * 8 + half * 4) = to_out4(a, bf16());
+        *reinterpret_cast<bf16x4*>(dV + db * 32 + jg * 8 + half * 4) = to_out4(b, bf16());
+      }
+  } else {
+    float* aK = p.dk_acc + (size_t)g * head_elems + (size_t)my_key * D;
+    float* aV = p.dv_acc + (size_t)g * head_elems + (size_t)my_key * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        floatx4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = dk[db][jg * 4 + e];
+          b[e] = dv[db][jg * 4 + e];
+        }
+        *reinterpret_cast<floatx4*>(aK + db * 32 + jg * 8 + half * 4) = a;
+        *reinterpret_cast<floatx4*>(aV + db * 32 + jg * 8 + half * 4) = b;
+      }
+  }
+}
+
+}  // namespace upipe

@@ -28,6 +28,7 @@ struct BwdParams {
   const T* dout;       // pool: [hc][S][D]
   const float* lse;    // caller lse rows of the chunk's first head, [hc][S]
   const float* Drow;   // pool: D = <dO, O> per row, [hc][S]
+  const float* lse2;   // pool: lse * log2(e) per row, [hc][S]
   T* dq;               // pool: [hc][S][D]
   float* dk_acc;       // pool: fp32 partial dK over earlier chunks, [nkv][S][D] (or null)
   float* dv_acc;

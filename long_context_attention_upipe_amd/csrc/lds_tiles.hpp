@@ -1,0 +1,89 @@
+// bf16 tiles in LDS for gfx950: row-major, XOR-swizzled 16-byte chunks,
+// filled straight from global memory (global_load_lds_dwordx4, no register
+// staging), read either as row fragments (ds_read_b128) or as transposed
+// fragments (ds_read_b64_tr_b16), so one copy of a tile serves both MFMA
+// operand orientations.
+#pragma once
+
+#include "common.hpp"
+
+namespace upipe {
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Chunk c (16 bytes = 8 bf16) of row r lives at chunk position c ^ swz(r).
+// swz takes distinct values mod 8 over any 8 consecutive rows (row-fragment
+// reads: 8 lanes, 8 rows, one chunk each) and distinct values of swz >> 1
+// over each aligned group of 4 rows (transposed reads: 4 rows x 2 adjacent
+// chunks per 16 lanes), so both read patterns spread over the banks.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Element offset of chunk `chunk` of row `row` in a tile with D-element rows.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return row * D + ((chunk ^ swz(row)) << 3);
+}
+
+// Row fragment: elements [8*chunk, 8*chunk + 8) of `row`.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_row_frag(const bf16* tile, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(tile + tile_off<D>(row, chunk));
+}
+
+// Transposed fragment for an MFMA A/B operand whose contraction runs over the
+// tile's rows: lane (m = lane & 31, half = lane >> 5) receives
+//   X[rbase + c_row(e, half)][col0 + m],  e = 0..7,
+// i.e. the 16 rows rbase..rbase+15 in the k-order of a P/dS fragment built
+// from C registers 0..7 (or 8..15 with rbase + 16). Each of the two
+// ds_read_b64_tr_b16 gathers 4 rows: within a 16-lane group, lane i gets
+// element i & 3 of the 8-byte slot addressed by lane (i >> 2) + 4k as its
+// k-th value, so lane j addresses row 4*half + (j >> 2), columns 4*(j & 3)..+3.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_tr_frag(const bf16* tile, int rbase, int col0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int half = g >> 1, m0 = (g & 1) << 4;
+  const int row = rbase + (half << 2) + (j >> 2);
+  const int col = col0 + m0 + ((j & 3) << 2);
+  const int chunk = col >> 3, sub = col & 7;
+  const bf16* p0 = tile + row * D + ((chunk ^ swz(row)) << 3) + sub;
+  const bf16* p1 = tile + (row + 8) * D + ((chunk ^ swz(row + 8)) << 3) + sub;
+  const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p0);
+  const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p1);
+  const short8v c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// Issue the copy of rows g_row0 .. g_row0 + ROWS - 1 of a [S][D] bf16 matrix
+// into `tile` (rows past S - 1 repeat row S - 1: callers mask them). Each wave
+// instruction fills 1 KiB of LDS, 16 bytes per lane, lane order; the lane
+// picks the global chunk that belongs at its LDS position. Asynchronous:
+// complete with wait_vm() and a barrier before reading.
+template <int D, int ROWS, int NWAVES>
+__device__ __forceinline__ void tile_load_async(bf16* tile, const bf16* g, int g_row0, int S, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int SLOTS = ROWS * CPR;
+  constexpr int INSTR = SLOTS / 64;
+  static_assert(SLOTS % 64 == 0, "tile must be a whole number of 1 KiB wave copies");
+  static_assert(INSTR % NWAVES == 0, "wave copies must split evenly");
+#pragma unroll
+  for (int k = 0; k < INSTR / NWAVES; ++k) {
+    const int i = k * NWAVES + wave;
+    const int slot = i * 64 + lane;
+    const int r = slot / CPR, pos = slot % CPR;
+    const int c = pos ^ swz(r);
+    const int gr = min(g_row0 + r, S - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)gr * D + c * 8), (lds_void*)(tile + i * 512), 16, 0,
+                                     0);
+  }
+}
+
+// Wait for this wave's outstanding global loads (including LDS copies).
+__device__ __forceinline__ void wait_vm() {
+  // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+}  // namespace upipe

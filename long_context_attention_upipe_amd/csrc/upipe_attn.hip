@@ -19,6 +19,9 @@
 #include <vector>
 
 #include "../../include/upipe_attn.h"
+#include <type_traits>
+
+#include "attn_bf16.hpp"
 #include "attn_bwd.hpp"
 #include "attn_fwd.hpp"
 #include "copy_kernels.hpp"
@@ -122,7 +125,7 @@ FwdPool fwd_pool(const Problem& pr) {
 }
 
 struct BwdPool {
-  size_t q, dout, dq, k, v, drow, dk_acc, dv_acc, total;
+  size_t q, dout, dq, k, v, drow, lse2, dk_acc, dv_acc, total;
   bool has_acc;
 };
 BwdPool bwd_pool(const Problem& pr) {
@@ -135,6 +138,7 @@ BwdPool bwd_pool(const Problem& pr) {
   p.k = off; off += align_up(pr.nkv * U);
   p.v = off; off += align_up(pr.nkv * U);
   p.drow = off; off += align_up((size_t)pr.hc * pr.S * 4);
+  p.lse2 = off; off += align_up((size_t)pr.hc * pr.S * 4);
   p.has_acc = pr.hc < pr.G;
   const size_t A = (size_t)pr.S * pr.d * 4;
   p.dk_acc = off; off += p.has_acc ? align_up(A) : 0;
@@ -263,7 +267,10 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     fp.causal = pr.causal;
     fp.scale_log2 = scale * kLog2e;
     timed(K_FWD, st, [&] {
-      hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, fp);
+      if constexpr (std::is_same<T, bf16>::value)
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, fp);
+      else
+        hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, fp);
     });
     timed(K_UNPACK, st, [&] {
       hipLaunchKernelGGL(unpack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)Oc, (uint4*)out, S,
@@ -286,6 +293,7 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
   T* Kc = reinterpret_cast<T*>(ws + pool.k);
   T* Vc = reinterpret_cast<T*>(ws + pool.v);
   float* Dc = reinterpret_cast<float*>(ws + pool.drow);
+  float* L2c = reinterpret_cast<float*>(ws + pool.lse2);
   float* dKa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dk_acc) : nullptr;
   float* dVa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dv_acc) : nullptr;
   const int n_qtiles = (S + DqShape<T, D>::BQ - 1) / DqShape<T, D>::BQ;
@@ -313,8 +321,8 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     const unsigned pre_grid =
         (unsigned)std::min<size_t>((rows + kRowsPerPreBlock - 1) / kRowsPerPreBlock, 256 * 32);
     timed(K_BWD_PRE, st, [&] {
-      hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st, (const T*)out, (const T*)dout, dOc,
-                         Dc, S, pr.Hq, c.q_head0, pr.hc);
+      hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st, (const T*)out, (const T*)dout, lse,
+                         dOc, Dc, L2c, S, pr.Hq, c.q_head0, pr.hc);
     });
 
     BwdParams<T> bp;
@@ -324,6 +332,7 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     bp.dout = dOc;
     bp.lse = lse + (size_t)c.q_head0 * S;
     bp.Drow = Dc;
+    bp.lse2 = L2c;
     bp.dq = dQc;
     bp.dk_acc = dKa;
     bp.dv_acc = dVa;
@@ -342,10 +351,16 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     bp.scale = scale;
     bp.scale_log2 = scale * kLog2e;
     timed(K_BWD_DKDV, st, [&] {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(n_ktiles * pr.nkv), dim3(256), 0, st, bp);
+      if constexpr (std::is_same<T, bf16>::value)
+        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D>), dim3(n_ktiles * pr.nkv), dim3(256), 0, st, bp);
+      else
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3(n_ktiles * pr.nkv), dim3(256), 0, st, bp);
     });
     timed(K_BWD_DQ, st, [&] {
-      hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, bp);
+      if constexpr (std::is_same<T, bf16>::value)
+        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, bp);
+      else
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, bp);
     });
     timed(K_UNPACK, st, [&] {
       hipLaunchKernelGGL(unpack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)dQc, (uint4*)dq, S,
