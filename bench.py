@@ -88,6 +88,7 @@ def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
     base = torch.cuda.memory_allocated(dev)
     q, k, v, do = make_inputs(w, device=dev)
     out = torch.empty_like(q)
+    out_lo = torch.empty_like(q) if q.dtype == torch.bfloat16 else None  # out's rounding residual, for D
     lse = torch.empty((w.Hq, w.S), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     code = up.dtype_code(q.dtype)
@@ -97,10 +98,10 @@ def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
     stream = torch.cuda.current_stream(dev)
 
     def fwd():
-        up.upipe_attn_fwd(q, k, v, out, lse, head_chunk, w.causal, ws, stream)
+        up.upipe_attn_fwd(q, k, v, out, out_lo, lse, head_chunk, w.causal, ws, stream)
 
     def bwd():
-        up.upipe_attn_bwd(q, k, v, out, do, lse, dq, dk, dv, head_chunk, w.causal, ws, stream)
+        up.upipe_attn_bwd(q, k, v, out, out_lo, do, lse, dq, dk, dv, head_chunk, w.causal, ws, stream)
 
     for _ in range(warmup):
         fwd()
@@ -155,7 +156,7 @@ def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
         "kernels": kernels,
     }
     tensors = (q, k, v, do)
-    del out, lse, dq, dk, dv, ws
+    del out, out_lo, lse, dq, dk, dv, ws
     return res, tensors
 
 

@@ -77,7 +77,8 @@ size_t upipe_attn_fwd_workspace_bytes(int64_t S, int Hq, int Hkv, int d,
 
 /*
  * Bytes of the fixed buffer pool that upipe_attn_bwd needs: the chunk's q, dout
- * and dq rows, its kv head(s), the per-row D = <dout, out> terms, and -- only
+ * and dq rows, its kv head(s), the per-row D = <dout, out> and lse*log2(e)
+ * terms, and -- only
  * when head_chunk < G, so that one kv head's gradient is summed over several
  * chunks -- fp32 dk/dv accumulators for one kv head.
  * Returns 0 and sets upipe_last_error() on invalid arguments.
@@ -88,26 +89,36 @@ size_t upipe_attn_bwd_workspace_bytes(int64_t S, int Hq, int Hkv, int d,
 /*
  * Forward. Reads q, k, v; writes out and lse (every element). Runs the head
  * chunks in ascending head order on `stream`, each through the same workspace.
+ *
+ * out_lo (bf16 only; may be NULL): receives, element by element, the bf16
+ * rounding residual of out, bf16(o - out) where o is the fp32 result, same
+ * layout as out. Handing it to upipe_attn_bwd lets the backward form
+ * D = <dout, o> from o to about 16 significant bits instead of 8. That
+ * matters for rows whose softmax is peaked (every causal row near the start
+ * of the sequence): there dP_ij - D_i cancels and a D taken from the rounded
+ * out alone can lose most of the gradient's accuracy. Ignored for fp32.
  */
 int upipe_attn_fwd(const void* q, const void* k, const void* v,
-                   void* out, float* lse,
+                   void* out, void* out_lo, float* lse,
                    int64_t S, int Hq, int Hkv, int d, int head_chunk,
                    int causal, int dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward (recompute-based: the probabilities are rebuilt from q, k and the
- * saved lse instead of being stored). Inputs: q, k, v, the forward's out and
- * lse, and the upstream gradient dout. Writes dq, dk, dv (every element;
- * overwritten, not accumulated into):
- *   D_hi  = <dout_hi, out_hi>,  P_ij = exp(s_ij - lse_hi)
+ * saved lse instead of being stored). Inputs: q, k, v, the forward's out,
+ * out_lo (may be NULL: D then comes from out alone) and lse, and the upstream
+ * gradient dout. Writes dq, dk, dv (every element; overwritten, not
+ * accumulated into):
+ *   D_hi  = <dout_hi, out_hi + out_lo_hi>,  P_ij = exp(s_ij - lse_hi)
  *   dS_ij = P_ij (<dout_hi, v_gj> - D_hi)
  *   dq_hi = tau sum_j dS_ij k_gj
  *   dk_gj = tau sum_{h in group g} sum_i dS_ij q_hi
  *   dv_gj = sum_{h in group g} sum_i P_ij dout_hi
  */
 int upipe_attn_bwd(const void* q, const void* k, const void* v,
-                   const void* out, const void* dout, const float* lse,
+                   const void* out, const void* out_lo, const void* dout,
+                   const float* lse,
                    void* dq, void* dk, void* dv,
                    int64_t S, int Hq, int Hkv, int d, int head_chunk,
                    int causal, int dtype,

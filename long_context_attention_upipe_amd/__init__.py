@@ -35,22 +35,26 @@ def workspace(S, Hq, Hkv, d, head_chunk, dtype, device="cuda", which="both"):
     return torch.empty(max(sizes), dtype=torch.uint8, device=device)
 
 
-def attention_forward(q, k, v, head_chunk=1, causal=True, ws=None, stream=None):
-    """out, lse = attention over [S,Hq,d] / [S,Hkv,d] device tensors."""
+def attention_forward(q, k, v, head_chunk=1, causal=True, ws=None, stream=None, residual=True):
+    """(out, lse, out_lo) of attention over [S,Hq,d] / [S,Hkv,d] device tensors.
+
+    out_lo is out's bf16 rounding residual (None for fp32 or residual=False);
+    pass it to attention_backward for an accurate D = <dout, out>."""
     import torch
 
     S, Hq, d = q.shape
     Hkv = k.shape[1]
     out = torch.empty_like(q)
+    out_lo = torch.empty_like(q) if (residual and q.dtype == torch.bfloat16) else None
     lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device)
     if ws is None:
         ws = workspace(S, Hq, Hkv, d, head_chunk, q.dtype, q.device, "fwd")
-    upipe_attn_fwd(q, k, v, out, lse, head_chunk, causal, ws, stream)
-    return out, lse
+    upipe_attn_fwd(q, k, v, out, out_lo, lse, head_chunk, causal, ws, stream)
+    return out, lse, out_lo
 
 
-def attention_backward(q, k, v, out, dout, lse, head_chunk=1, causal=True, ws=None, stream=None):
-    """dq, dk, dv of attention given the forward's out and lse."""
+def attention_backward(q, k, v, out, dout, lse, out_lo=None, head_chunk=1, causal=True, ws=None, stream=None):
+    """dq, dk, dv of attention given the forward's out, lse (and out_lo)."""
     import torch
 
     S, Hq, d = q.shape
@@ -58,5 +62,5 @@ def attention_backward(q, k, v, out, dout, lse, head_chunk=1, causal=True, ws=No
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if ws is None:
         ws = workspace(S, Hq, Hkv, d, head_chunk, q.dtype, q.device, "bwd")
-    upipe_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, head_chunk, causal, ws, stream)
+    upipe_attn_bwd(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, ws, stream)
     return dq, dk, dv

@@ -45,9 +45,10 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_fwd_workspace_bytes.restype = sz
     L.upipe_attn_bwd_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
     L.upipe_attn_bwd_workspace_bytes.restype = sz
-    L.upipe_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.upipe_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     L.upipe_attn_fwd.restype = i32
-    L.upipe_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.upipe_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz,
+                                 vp]
     L.upipe_attn_bwd.restype = i32
     p32 = ctypes.POINTER(ctypes.c_int32)
     L.upipe_attn_plan.argtypes = [i32, i32, i32, i32, p32, p32, p32, p32]
@@ -115,7 +116,7 @@ def _stream_handle(stream):
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr())
+    return ctypes.c_void_p(None if t is None else t.data_ptr())
 
 
 def _shape(q, k):
@@ -134,24 +135,25 @@ def _require(ts, dt):
             raise UpipeError(-1, f"dtype mismatch: {t.dtype} vs {dt}")
 
 
-def upipe_attn_fwd(q, k, v, out, lse, head_chunk, causal, workspace, stream=None) -> None:
-    """Enqueue the forward on ``stream`` (default: torch's current stream)."""
+def upipe_attn_fwd(q, k, v, out, out_lo, lse, head_chunk, causal, workspace, stream=None) -> None:
+    """Enqueue the forward on ``stream`` (default: torch's current stream).
+    ``out_lo`` (bf16, like ``out``, or None) receives out's rounding residual."""
     S, Hq, Hkv, d = _shape(q, k)
-    _require((q, k, v, out), q.dtype)
+    _require((q, k, v, out) + ((out_lo,) if out_lo is not None else ()), q.dtype)
     _require((lse,), torch.float32)
     _require((workspace,), torch.uint8)
-    _check(lib().upipe_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), S, Hq, Hkv, d,
+    _check(lib().upipe_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(lse), S, Hq, Hkv, d,
                                 int(head_chunk), int(causal), dtype_code(q.dtype),
                                 _ptr(workspace), workspace.numel(), _stream_handle(stream)))
 
 
-def upipe_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, head_chunk, causal, workspace, stream=None) -> None:
+def upipe_attn_bwd(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, workspace, stream=None) -> None:
     """Enqueue the backward on ``stream`` (default: torch's current stream)."""
     S, Hq, Hkv, d = _shape(q, k)
-    _require((q, k, v, out, dout, dq, dk, dv), q.dtype)
+    _require((q, k, v, out, dout, dq, dk, dv) + ((out_lo,) if out_lo is not None else ()), q.dtype)
     _require((lse,), torch.float32)
     _require((workspace,), torch.uint8)
-    _check(lib().upipe_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+    _check(lib().upipe_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(dout), _ptr(lse),
                                 _ptr(dq), _ptr(dk), _ptr(dv), S, Hq, Hkv, d,
                                 int(head_chunk), int(causal), dtype_code(q.dtype),
                                 _ptr(workspace), workspace.numel(), _stream_handle(stream)))

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
   if (my_row < S) {
     const float inv = 1.f / l_tot;
     bf16* O = p.o + (size_t)hl * head_elems + (size_t)my_row * D;
+    bf16* Olo = p.o_lo ? p.o_lo + ((size_t)my_row * p.H + hl) * D : nullptr;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -143,7 +144,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
         floatx4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = o_acc[db][jg * 4 + e] * inv;
-        *reinterpret_cast<bf16x4*>(O + db * 32 + jg * 8 + half * 4) = to_out4(o4, bf16());
+        const bf16x4 hi = to_out4(o4, bf16());
+        *reinterpret_cast<bf16x4*>(O + db * 32 + jg * 8 + half * 4) = hi;
+        if (Olo) {
+          const floatx4 r = o4 - __builtin_convertvector(hi, floatx4);
+          *reinterpret_cast<bf16x4*>(Olo + db * 32 + jg * 8 + half * 4) = to_out4(r, bf16());
+        }
       }
     if (half == 0) p.lse[(size_t)hl * S + my_row] = (m_run + __log2f(l_tot)) * kLn2;
   }

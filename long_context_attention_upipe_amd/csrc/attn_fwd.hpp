@@ -30,6 +30,8 @@ struct FwdParams {
   const T* k;        // pool: chunk kv heads, [nkv][S][D]
   const T* v;        // pool: [nkv][S][D]
   T* o;              // pool: chunk output rows, [hc][S][D]
+  T* o_lo;           // caller out_lo at the chunk's first head (row stride H*D), or null
+  int H;             // caller heads per row (out_lo row stride in heads)
   float* lse;        // caller lse rows of the chunk's first head, [hc][S]
   int S;
   int hc;            // heads in the chunk

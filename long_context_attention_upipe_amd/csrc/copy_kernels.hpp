@@ -7,7 +7,8 @@
 //    ("Road to 5 Million Tokens" talk summary, Chapters: Ulysses exchanges
 //    activations between GPUs; batched heads reuse the previous batch's
 //    buffer).
-//  * bwd_pre: D_i = <dO_i, O_i> per row in fp32 from the stored output, the
+//  * bwd_pre: D_i = <dO_i, O_i> per row in fp32 from the stored output (plus
+//    its stored rounding residual when there is one), the
 //    chunk's dO rows packed, and lse_i * log2(e) (the base-2 exponent offset
 //    the backward kernels use), all in one pass.
 #pragma once
@@ -45,7 +46,8 @@ __global__ __launch_bounds__(256) void unpack_heads_kernel(const uint4* __restri
 // One group of D/EPV lanes per (row, head): reads a 16-byte slice of out and
 // dout each, writes the dout slice into the pool, reduces the dot product.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out, const T* __restrict__ dout,
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out, const T* __restrict__ out_lo,
+                                                     const T* __restrict__ dout,
                                                      const float* __restrict__ lse, T* __restrict__ dout_pool,
                                                      float* __restrict__ Drow, float* __restrict__ lse2, int S,
                                                      int H, int h0, int nh) {
@@ -61,11 +63,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
     const uint4 ov = *reinterpret_cast<const uint4*>(out + src);
     const uint4 dv = *reinterpret_cast<const uint4*>(dout + src);
     *reinterpret_cast<uint4*>(dout_pool + ((size_t)hl * S + i) * D + sub * EPV) = dv;
+    const uint4 lv = out_lo ? *reinterpret_cast<const uint4*>(out_lo + src) : uint4{0, 0, 0, 0};
     const T* oe = reinterpret_cast<const T*>(&ov);
+    const T* le = reinterpret_cast<const T*>(&lv);
     const T* de = reinterpret_cast<const T*>(&dv);
     float acc = 0.f;
+    // out + out_lo is exact in fp32 (two 8-bit-mantissa parts, 2^-9 apart)
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) acc = fmaf(to_f32(oe[e]), to_f32(de[e]), acc);
+    for (int e = 0; e < EPV; ++e) acc = fmaf(to_f32(oe[e]) + to_f32(le[e]), to_f32(de[e]), acc);
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (sub == 0) {

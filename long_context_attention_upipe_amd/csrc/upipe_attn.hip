@@ -226,8 +226,8 @@ int check_launch(const char* what) {
 }
 
 template <typename T, int D>
-int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* out, float* lse, char* ws,
-            hipStream_t st) {
+int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* out, void* out_lo, float* lse,
+            char* ws, hipStream_t st) {
   const FwdPool pool = fwd_pool(pr);
   const int S = (int)pr.S;
   const int vpr = D * (int)sizeof(T) / 16;
@@ -259,6 +259,8 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     fp.k = Kc;
     fp.v = Vc;
     fp.o = Oc;
+    fp.o_lo = out_lo ? reinterpret_cast<T*>(out_lo) + (size_t)c.q_head0 * D : nullptr;
+    fp.H = pr.Hq;
     fp.lse = lse + (size_t)c.q_head0 * S;
     fp.S = S;
     fp.hc = pr.hc;
@@ -282,8 +284,8 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
 }
 
 template <typename T, int D>
-int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, const void* out, const void* dout,
-            const float* lse, void* dq, void* dk, void* dv, char* ws, hipStream_t st) {
+int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, const void* out, const void* out_lo,
+            const void* dout, const float* lse, void* dq, void* dk, void* dv, char* ws, hipStream_t st) {
   const BwdPool pool = bwd_pool(pr);
   const int S = (int)pr.S;
   const int vpr = D * (int)sizeof(T) / 16;
@@ -321,7 +323,7 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     const unsigned pre_grid =
         (unsigned)std::min<size_t>((rows + kRowsPerPreBlock - 1) / kRowsPerPreBlock, 256 * 32);
     timed(K_BWD_PRE, st, [&] {
-      hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st, (const T*)out, (const T*)dout, lse,
+      hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st, (const T*)out, (const T*)out_lo, (const T*)dout, lse,
                          dOc, Dc, L2c, S, pr.Hq, c.q_head0, pr.hc);
     });
 
@@ -392,9 +394,9 @@ size_t upipe_attn_bwd_workspace_bytes(int64_t S, int Hq, int Hkv, int d, int hea
   return bwd_pool(pr).total;
 }
 
-int upipe_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t S, int Hq, int Hkv,
-                   int d, int head_chunk, int causal, int dtype, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+int upipe_attn_fwd(const void* q, const void* k, const void* v, void* out, void* out_lo, float* lse, int64_t S,
+                   int Hq, int Hkv, int d, int head_chunk, int causal, int dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   Problem pr;
   if (int rc = validate(S, Hq, Hkv, d, head_chunk, causal, dtype, &pr)) return rc;
   const void* ptrs[] = {q, k, v, out, lse, workspace};
@@ -403,6 +405,8 @@ int upipe_attn_fwd(const void* q, const void* k, const void* v, void* out, float
     if (!ptrs[i]) return fail(UPIPE_EINVAL, "%s is NULL", names[i]);
     if (!aligned16(ptrs[i])) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", names[i]);
   }
+  if (out_lo && !aligned16(out_lo)) return fail(UPIPE_EINVAL, "out_lo is not 16-byte aligned");
+  if (dtype != UPIPE_BF16) out_lo = nullptr;  // fp32 outputs carry no rounding residual
   const size_t need = fwd_pool(pr).total;
   if (workspace_bytes < need)
     return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
@@ -410,16 +414,17 @@ int upipe_attn_fwd(const void* q, const void* k, const void* v, void* out, float
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == UPIPE_BF16) {
-    if (d == 128) return run_fwd<bf16, 128>(pr, q, k, v, out, lse, ws, st);
-    return run_fwd<bf16, 64>(pr, q, k, v, out, lse, ws, st);
+    if (d == 128) return run_fwd<bf16, 128>(pr, q, k, v, out, out_lo, lse, ws, st);
+    return run_fwd<bf16, 64>(pr, q, k, v, out, out_lo, lse, ws, st);
   }
-  if (d == 128) return run_fwd<float, 128>(pr, q, k, v, out, lse, ws, st);
-  return run_fwd<float, 64>(pr, q, k, v, out, lse, ws, st);
+  if (d == 128) return run_fwd<float, 128>(pr, q, k, v, out, out_lo, lse, ws, st);
+  return run_fwd<float, 64>(pr, q, k, v, out, out_lo, lse, ws, st);
 }
 
-int upipe_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-                   void* dq, void* dk, void* dv, int64_t S, int Hq, int Hkv, int d, int head_chunk, int causal,
-                   int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+int upipe_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* out_lo,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv, int64_t S, int Hq, int Hkv,
+                   int d, int head_chunk, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   Problem pr;
   if (int rc = validate(S, Hq, Hkv, d, head_chunk, causal, dtype, &pr)) return rc;
   const void* ptrs[] = {q, k, v, out, dout, lse, dq, dk, dv, workspace};
@@ -428,6 +433,8 @@ int upipe_attn_bwd(const void* q, const void* k, const void* v, const void* out,
     if (!ptrs[i]) return fail(UPIPE_EINVAL, "%s is NULL", names[i]);
     if (!aligned16(ptrs[i])) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", names[i]);
   }
+  if (out_lo && !aligned16(out_lo)) return fail(UPIPE_EINVAL, "out_lo is not 16-byte aligned");
+  if (dtype != UPIPE_BF16) out_lo = nullptr;
   const size_t need = bwd_pool(pr).total;
   if (workspace_bytes < need)
     return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
@@ -435,11 +442,11 @@ int upipe_attn_bwd(const void* q, const void* k, const void* v, const void* out,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == UPIPE_BF16) {
-    if (d == 128) return run_bwd<bf16, 128>(pr, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
-    return run_bwd<bf16, 64>(pr, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+    if (d == 128) return run_bwd<bf16, 128>(pr, q, k, v, out, out_lo, dout, lse, dq, dk, dv, ws, st);
+    return run_bwd<bf16, 64>(pr, q, k, v, out, out_lo, dout, lse, dq, dk, dv, ws, st);
   }
-  if (d == 128) return run_bwd<float, 128>(pr, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
-  return run_bwd<float, 64>(pr, q, k, v, out, dout, lse, dq, dk, dv, ws, st);
+  if (d == 128) return run_bwd<float, 128>(pr, q, k, v, out, out_lo, dout, lse, dq, dk, dv, ws, st);
+  return run_bwd<float, 64>(pr, q, k, v, out, out_lo, dout, lse, dq, dk, dv, ws, st);
 }
 
 int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks, int32_t* q_head0, int32_t* kv_head0,

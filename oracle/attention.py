@@ -67,8 +67,8 @@ __all__ = [
     "backward_cols_dkdv",
 ]
 
-# Upper bound on the number of float64 score elements held at once.
-_SCORE_BUDGET = 1 << 24
+# Upper bound on the number of float64 score elements held at once (512 MiB).
+_SCORE_BUDGET = 1 << 26
 
 
 def _f64(x) -> np.ndarray:
@@ -90,11 +90,12 @@ def _look_back_mask(rows: np.ndarray, n_cols: int, causal: bool) -> np.ndarray |
 
 
 def _softmax_rows(s: np.ndarray):
-    """Row max, exp and row sum of a score block (masked entries are -inf)."""
-    m = s.max(axis=1)
-    e = np.exp(s - m[:, None])
-    l = e.sum(axis=1)
-    return e / l[:, None], m + np.log(l)
+    """Max, exp and sum along the last (key) axis of a score block (masked
+    entries are -inf). Returns (P, LSE)."""
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=-1, keepdims=True)
+    return e / l, (m + np.log(l))[..., 0]
 
 
 def attention_forward(q, k, v, causal: bool = True, block: int = 256):
@@ -156,46 +157,66 @@ def attention_backward(q, k, v, dout, causal: bool = True, block: int = 256):
     return dq, dk, dv
 
 
-def _row_batches(rows: np.ndarray, S: int, causal: bool):
-    """Split sorted row indices into batches whose score block fits the budget."""
+def _row_batches(rows: np.ndarray, S: int, causal: bool, heads: int = 1):
+    """Split sorted row indices into batches whose score block (rows x heads x
+    keys) fits the budget."""
     order = np.argsort(rows, kind="stable")
     start, n = 0, len(order)
     while start < n:
         end = start + 1
         while end < n:
             width = int(rows[order[end]]) + 1 if causal else S
-            if (end - start + 1) * width > _SCORE_BUDGET:
+            if (end - start + 1) * heads * width > _SCORE_BUDGET:
                 break
             end += 1
         yield order[start:end]
         start = end
 
 
+def _group_scores(q_blk, k_g, tau, mask):
+    """tau * <q, k> for a batch of rows and every query head of one kv group.
+
+    q_blk [R, G, d], k_g [n, d] -> scores [R, G, n], with -inf where ``mask``
+    [R, n] says the key is outside the row's look-back set.
+    """
+    R, G, d = q_blk.shape
+    s = (tau * (q_blk.reshape(R * G, d) @ k_g.T)).reshape(R, G, -1)
+    if mask is not None:
+        s[np.broadcast_to(mask[:, None, :], s.shape)] = -np.inf
+    return s
+
+
+def _rows_matmul(a, b):
+    """[R, G, n] @ [n, m] -> [R, G, m] as one 2-D matrix product."""
+    R, G, n = a.shape
+    return (a.reshape(R * G, n) @ b).reshape(R, G, b.shape[1])
+
+
 def forward_rows(q_rows, k, v, rows, causal: bool = True):
     """Exact O and LSE at selected query rows, O(S*d) work per row.
 
-    ``q_rows`` [R,Hq,d] holds the query vectors of positions ``rows``.
+    ``q_rows`` [R,Hq,d] holds the query vectors of positions ``rows``. The
+    query heads that share a kv head are scored together against it.
     Returns (out_rows [R,Hq,d], lse_rows [Hq,R]) in float64, in ``rows`` order.
     """
     q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
     rows = np.asarray(rows, dtype=np.int64)
     S, Hkv, d = k.shape
     Hq = q_rows.shape[1]
+    G = Hq // Hkv
     tau = 1.0 / math.sqrt(d)
     out = np.zeros((len(rows), Hq, d))
     lse = np.zeros((Hq, len(rows)))
-    for sel in _row_batches(rows, S, causal):
+    for sel in _row_batches(rows, S, causal, G):
         r = rows[sel]
         n_cols = int(r.max()) + 1 if causal else S
         mask = _look_back_mask(r, n_cols, causal)
-        for h in range(Hq):
-            g = kv_head_of(h, Hq, Hkv)
-            s = tau * (q_rows[sel, h, :] @ k[:n_cols, g, :].T)
-            if mask is not None:
-                s[mask] = -np.inf
+        for g in range(Hkv):
+            hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]
+            s = _group_scores(q_rows[sel][:, hs, :], k[:n_cols, g, :], tau, mask)
             p, lse_blk = _softmax_rows(s)
-            out[sel, h, :] = p @ v[:n_cols, g, :]
-            lse[h, sel] = lse_blk
+            out[np.ix_(sel, hs)] = _rows_matmul(p, v[:n_cols, g, :])
+            lse[np.ix_(hs, sel)] = lse_blk.T
     return out, lse
 
 
@@ -210,23 +231,23 @@ def backward_rows_dq(q_rows, k, v, dout_rows, rows, causal: bool = True):
     rows = np.asarray(rows, dtype=np.int64)
     S, Hkv, d = k.shape
     Hq = q_rows.shape[1]
+    G = Hq // Hkv
     tau = 1.0 / math.sqrt(d)
     dq = np.zeros((len(rows), Hq, d))
-    for sel in _row_batches(rows, S, causal):
+    for sel in _row_batches(rows, S, causal, G):
         r = rows[sel]
         n_cols = int(r.max()) + 1 if causal else S
         mask = _look_back_mask(r, n_cols, causal)
-        for h in range(Hq):
-            g = kv_head_of(h, Hq, Hkv)
-            s = tau * (q_rows[sel, h, :] @ k[:n_cols, g, :].T)
-            if mask is not None:
-                s[mask] = -np.inf
+        for g in range(Hkv):
+            hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]
+            s = _group_scores(q_rows[sel][:, hs, :], k[:n_cols, g, :], tau, mask)
             p, _ = _softmax_rows(s)
-            o = p @ v[:n_cols, g, :]
-            D = (dout_rows[sel, h, :] * o).sum(axis=1)
-            dp = dout_rows[sel, h, :] @ v[:n_cols, g, :].T
-            ds = p * (dp - D[:, None])
-            dq[sel, h, :] = tau * (ds @ k[:n_cols, g, :])
+            o = _rows_matmul(p, v[:n_cols, g, :])
+            do_blk = dout_rows[sel][:, hs, :]
+            D = (do_blk * o).sum(axis=-1)
+            dp = _rows_matmul(do_blk, v[:n_cols, g, :].T)
+            ds = p * (dp - D[..., None])
+            dq[np.ix_(sel, hs)] = tau * _rows_matmul(ds, k[:n_cols, g, :])
     return dq
 
 

@@ -11,6 +11,24 @@ if TESTS not in sys.path:
     sys.path.insert(0, TESTS)
 
 
+def _keep_freed_heap_memory():
+    """The oracle allocates and frees score blocks of hundreds of MiB; keep
+    freed memory in the process instead of unmapping it, so the next block
+    does not page-fault all over again (glibc mallopt: mmap and trim
+    thresholds)."""
+    try:
+        import ctypes
+
+        libc = ctypes.CDLL("libc.so.6")
+        libc.mallopt(-3, 1 << 30)       # M_MMAP_THRESHOLD
+        libc.mallopt(-1, (1 << 31) - 1)  # M_TRIM_THRESHOLD
+    except (OSError, AttributeError):
+        pass
+
+
+_keep_freed_heap_memory()
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: multi-minute GPU case (full-size workloads)")

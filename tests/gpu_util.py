@@ -21,10 +21,10 @@ def run(q, k, v, do, head_chunk, causal=True, ws=None):
     Hkv = k.shape[1]
     if ws is None:
         ws = up.workspace(S, Hq, Hkv, d, head_chunk, q.dtype, q.device, "both")
-    out, lse = up.attention_forward(q, k, v, head_chunk=head_chunk, causal=causal, ws=ws)
+    out, lse, out_lo = up.attention_forward(q, k, v, head_chunk=head_chunk, causal=causal, ws=ws)
     res = {"out": out, "lse": lse}
     if do is not None:
-        dq, dk, dv = up.attention_backward(q, k, v, out, do, lse, head_chunk=head_chunk, causal=causal, ws=ws)
+        dq, dk, dv = up.attention_backward(q, k, v, out, do, lse, out_lo, head_chunk=head_chunk, causal=causal, ws=ws)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return res

@@ -77,23 +77,26 @@ def test_pool_at_5m_tokens_matches_plan():
     gib = 1 << 30
     sizes = [L.upipe_attn_bwd_workspace_bytes(5242880, 8, 1, 128, hc, 0) / gib for hc in (1, 2, 4, 8)]
     U = 5242880 * 128 * 2 / gib
-    expect = [3 * hc * U + 2 * U + hc * 5242880 * 4 / gib + (4 * U if hc < 8 else 0) for hc in (1, 2, 4, 8)]
+    # q, dO, dq rows of the chunk; k, v; D and lse*log2(e) per row; fp32 dk/dv when a group spans chunks
+    expect = [3 * hc * U + 2 * U + 2 * hc * 5242880 * 4 / gib + (4 * U if hc < 8 else 0) for hc in (1, 2, 4, 8)]
     for got, exp in zip(sizes, expect):
         assert abs(got - exp) < 1e-3
 
 
 def _fwd(**kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, S=256, Hq=4, Hkv=1, d=128, hc=1, causal=1, dtype=0,
-             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, out_lo=None, lse=FAKE, S=256, Hq=4, Hkv=1, d=128, hc=1, causal=1,
+             dtype=0, ws=FAKE, ws_bytes=1 << 40, stream=None)
     a.update(kw)
-    return L.lib().upipe_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["S"], a["Hq"], a["Hkv"], a["d"],
+    return L.lib().upipe_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["out_lo"], a["lse"], a["S"], a["Hq"], a["Hkv"],
+                                  a["d"],
                                   a["hc"], a["causal"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def _bwd(**kw):
-    a = dict(S=256, Hq=4, Hkv=1, d=128, hc=1, causal=1, dtype=0, ws_bytes=1 << 40, dq=FAKE)
+    a = dict(S=256, Hq=4, Hkv=1, d=128, hc=1, causal=1, dtype=0, ws_bytes=1 << 40, dq=FAKE, out_lo=None)
     a.update(kw)
-    return L.lib().upipe_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["dq"], FAKE, FAKE, a["S"], a["Hq"], a["Hkv"],
+    return L.lib().upipe_attn_bwd(FAKE, FAKE, FAKE, FAKE, a["out_lo"], FAKE, FAKE, a["dq"], FAKE, FAKE, a["S"], a["Hq"],
+                                  a["Hkv"],
                                   a["d"], a["hc"], a["causal"], a["dtype"], FAKE, a["ws_bytes"], None)
 
 
@@ -110,6 +113,7 @@ def _bwd(**kw):
     (dict(lse=None), -1, "lse is NULL"),
     (dict(out=ctypes.c_void_p(0x10008)), -1, "not 16-byte aligned"),
     (dict(ws_bytes=1024), -3, "workspace too small"),
+    (dict(out_lo=ctypes.c_void_p(0x10004)), -1, "out_lo is not 16-byte aligned"),
 ])
 def test_forward_rejects_bad_arguments(kw, status, msg):
     assert _fwd(**kw) == status
@@ -121,6 +125,7 @@ def test_forward_rejects_bad_arguments(kw, status, msg):
     (dict(dq=None), -1, "dq is NULL"),
     (dict(ws_bytes=0), -3, "workspace too small"),
     (dict(d=32), -2, "head dim"),
+    (dict(out_lo=ctypes.c_void_p(0x10002)), -1, "out_lo is not 16-byte aligned"),
 ])
 def test_backward_rejects_bad_arguments(kw, status, msg):
     assert _bwd(**kw) == status

@@ -15,17 +15,19 @@ MUTATIONS = {
     "scale_1_over_d": ("tau = 1.0 / math.sqrt(d)", "tau = 1.0 / d"),
     "diagonal_excluded": ("np.arange(n_cols)[None, :] > rows[:, None]", "np.arange(n_cols)[None, :] >= rows[:, None]"),
     "gqa_modulo_mapping": ("return h // (n_q_heads // n_kv_heads)", "return h % n_kv_heads"),
-    "lse_base2": ("return e / l[:, None], m + np.log(l)", "return e / l[:, None], m + np.log2(l)"),
-    "lse_missing_max": ("return e / l[:, None], m + np.log(l)", "return e / l[:, None], np.log(l)"),
+    "lse_base2": ("return e / l, (m + np.log(l))[..., 0]", "return e / l, (m + np.log2(l))[..., 0]"),
+    "lse_missing_max": ("return e / l, (m + np.log(l))[..., 0]", "return e / l, (np.log(l))[..., 0]"),
     "bwd_missing_D": ("ds = p * (dp - D[:, None])", "ds = p * dp"),
     "bwd_dk_missing_tau": ("dk[:n_cols, g, :] += tau * (ds.T @ q_blk)", "dk[:n_cols, g, :] += (ds.T @ q_blk)"),
     "bwd_dv_uses_ds": ("dv[:n_cols, g, :] += p.T @ do_blk", "dv[:n_cols, g, :] += ds.T @ do_blk"),
     "bwd_dq_transposed_k": ("dq[r0:r1, h, :] = tau * (ds @ k[:n_cols, g, :])", "dq[r0:r1, h, :] = tau * (ds @ v[:n_cols, g, :])"),
-    "rows_dq_missing_D": ("ds = p * (dp - D[:, None])\n            dq[sel", "ds = p * dp\n            dq[sel"),
     "cols_wrong_causal_side": ("(need[None, :] < cj[:, None])", "(need[None, :] > cj[:, None])"),
     "cols_dv_missing": ("dv[c0:c0 + per, g, :] += p @ doh", "dv[c0:c0 + per, g, :] += 0 * (p @ doh)"),
-    "fwd_rows_noncausal_width": ("n_cols = int(r.max()) + 1 if causal else S\n        mask = _look_back_mask(r, n_cols, causal)\n        for h in range(Hq):\n            g = kv_head_of(h, Hq, Hkv)\n            s = tau * (q_rows[sel, h, :] @ k[:n_cols, g, :].T)\n            if mask is not None:\n                s[mask] = -np.inf\n            p, lse_blk",
-                                 "n_cols = int(r.max()) + 1\n        mask = _look_back_mask(r, n_cols, causal)\n        for h in range(Hq):\n            g = kv_head_of(h, Hq, Hkv)\n            s = tau * (q_rows[sel, h, :] @ k[:n_cols, g, :].T)\n            if mask is not None:\n                s[mask] = -np.inf\n            p, lse_blk"),
+    "fwd_rows_noncausal_width": ("        n_cols = int(r.max()) + 1 if causal else S\n        mask = _look_back_mask(r, n_cols, causal)\n        for g in range(Hkv):\n            hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]\n            s = _group_scores(q_rows[sel][:, hs, :], k[:n_cols, g, :], tau, mask)\n            p, lse_blk",
+                                 "        n_cols = int(r.max()) + 1\n        mask = _look_back_mask(r, n_cols, causal)\n        for g in range(Hkv):\n            hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]\n            s = _group_scores(q_rows[sel][:, hs, :], k[:n_cols, g, :], tau, mask)\n            p, lse_blk"),
+    "rows_dq_missing_D": ("            ds = p * (dp - D[..., None])", "            ds = p * dp"),
+    "group_scores_mask_ignored": ("        s[np.broadcast_to(mask[:, None, :], s.shape)] = -np.inf", "        pass"),
+    "softmax_wrong_axis": ("    m = s.max(axis=-1, keepdims=True)", "    m = s.max(axis=0, keepdims=True)"),
 }
 
 
