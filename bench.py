@@ -42,6 +42,34 @@ ALGO_FLOPS_PER_PAIR_D = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 2}
 EXEC_FLOPS_PER_PAIR_D = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 6}
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources the library is built from."""
+    import hashlib
+
+    d = os.path.join(ROOT, "long_context_attention_upipe_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hpp", ".hip")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str, head_chunk: int):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE runs recorded in
+    profiles/traffic.json, or None if none were taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        entries = json.load(f).get("entries", [])
+    src = kernel_source_hash()
+    for e in entries:
+        if (e["kernel"], e["workload"], e["head_chunk"], e["src_sha256"]) == (kernel, workload, head_chunk, src):
+            return int(e["read_bytes_per_launch"] + e["write_bytes_per_launch"])
+    return None
+
+
 def pairs(S: int, causal: bool) -> int:
     return S * (S + 1) // 2 if causal else S * S
 
@@ -173,7 +201,7 @@ def roofline(w, res, head_chunk):
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": None,
+        "traffic": measured_traffic(name, w.name, head_chunk),
         "per_unit": f"{ALGO_FLOPS_PER_PAIR_D[name]}*d FLOP per unmasked (row, key) pair and head; "
                     f"{head_chunk} heads x S(S+1)/2 pairs per launch",
     }
