@@ -14,7 +14,8 @@ import torch
 
 _LIB_NAME = "libupipe_attn.so"
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, _LIB_NAME)
+# UPIPE_ATTN_LIBRARY may name another build of the same library (same ABI).
+LIB_PATH = os.environ.get("UPIPE_ATTN_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
 
 UPIPE_BF16 = 0
 UPIPE_FP32 = 1

@@ -83,13 +83,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
       }
       const bool need_mask = (p.causal && key0 + BK - 1 > wrow0) || (key0 + BK > S);
       if (need_mask) {
+        // key of register j = key0 + 32b + 4half + kj(j); keep it iff kj(j) <= lim
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b) {
+          const int kb = key0 + b * 32 + half * 4;
+          const int lim = p.causal ? min(my_row - kb, S - 1 - kb) : S - 1 - kb;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = key0 + b * 32 + c_row(j, half);
-            if ((p.causal && key > my_row) || key >= S) s[b][j] = NEG_INF;
-          }
+          for (int j = 0; j < 16; ++j)
+            if (c_row(j, 0) > lim) s[b][j] = NEG_INF;
+        }
       }
       float mx = NEG_INF;
 #pragma unroll
@@ -223,14 +225,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
           mma32(s, tile_row_frag<D>(sK[cur], b * 32 + col, 2 * ks + half), qf[ks]);
           mma32(dp, tile_row_frag<D>(sV[cur], b * 32 + col, 2 * ks + half), df[ks]);
         }
+        if (need_mask) {
+          // key of register j = key0 + 32b + 4half + kj(j); keep it iff kj(j) <= lim
+          const int kb = key0 + b * 32 + half * 4;
+          const int lim = p.causal ? min(my_row - kb, S - 1 - kb) : S - 1 - kb;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2));
-          if (need_mask) {
-            const int key = key0 + b * 32 + c_row(j, half);
-            if ((p.causal && key > my_row) || key >= S) pij = 0.f;
+          for (int j = 0; j < 16; ++j) {
+            const float pij = c_row(j, 0) <= lim ? __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2)) : 0.f;
+            s[j] = pij * (dp[j] - Dr);  // dS^T
           }
-          s[j] = pij * (dp[j] - Dr);  // dS^T
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2));
+            s[j] = pij * (dp[j] - Dr);  // dS^T
+          }
         }
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -357,6 +366,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
         mma32(dp, tile_row_frag<D>(sO[cur], col, 2 * ks + half), tile_row_frag<D>(sV, wave * 32 + col, 2 * ks + half));
       }
       const bool need_mask = (p.causal && r0 < wkey0 + 31) || (r0 + BQ > S);
+      // row of register j = r0 + 4half + kj(j); it counts iff lo <= kj(j) <= hi
+      const int rb = r0 + half * 4;
+      const int lo = need_mask && p.causal ? my_key - rb : 0;
+      const int hi = need_mask ? S - 1 - rb : 31;
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         const floatx4 l4 = *reinterpret_cast<const floatx4*>(&sLD[cur][jg * 8 + half * 4]);
@@ -364,11 +377,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = jg * 4 + e;
-          float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l4[e]));
-          if (need_mask) {
-            const int row = r0 + c_row(j, half);
-            if ((p.causal && my_key > row) || row >= S) pij = 0.f;
-          }
+          const int kj = c_row(j, 0);
+          const float pe = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l4[e]));
+          const float pij = (kj >= lo && kj <= hi) ? pe : 0.f;
           s[j] = pij;
           dp[j] = pij * (dp[j] - d4[e]);
         }
