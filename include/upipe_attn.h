@@ -151,6 +151,10 @@ int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks,
 int upipe_profile_enable(int on);
 int upipe_profile_read(int max_kernels, const char** names, int64_t* launches, double* total_ms);
 void upipe_profile_reset(void);
+/* Non-blocking: how many kernels bracketed since the last read/reset have
+ * finished, and (if `total` is not NULL) how many were bracketed. Lets a
+ * caller report progress of a long asynchronous call as kernels complete. */
+int upipe_profile_completed(int* total);
 
 /* Message for the last failed call on this thread ("" if none). Valid until
  * the next call into the library on the same thread. */

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     upipe_attn_fwd_workspace_bytes,
     upipe_attn_plan,
     upipe_last_error,
+    upipe_profile_completed,
     upipe_profile_enable,
     upipe_profile_read,
     upipe_profile_reset,

@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.upipe_profile_read.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_double)]
     L.upipe_profile_read.restype = i32
+    L.upipe_profile_completed.argtypes = [ctypes.POINTER(ctypes.c_int)]
+    L.upipe_profile_completed.restype = i32
     L.upipe_profile_reset.argtypes = []
     L.upipe_profile_reset.restype = None
     L.upipe_last_error.argtypes = []
@@ -179,3 +181,10 @@ def upipe_profile_read():
     if n < 0:
         raise UpipeError(n, upipe_last_error())
     return {names[i].decode(): (int(launches[i]), float(ms[i])) for i in range(min(n, n_max))}
+
+
+def upipe_profile_completed():
+    """(kernels finished, kernels bracketed) since the last read/reset; non-blocking."""
+    total = ctypes.c_int(0)
+    done = lib().upipe_profile_completed(ctypes.byref(total))
+    return int(done), int(total.value)

@@ -486,6 +486,16 @@ int upipe_profile_read(int max_kernels, const char** names, int64_t* launches, d
   return n;
 }
 
+int upipe_profile_completed(int* total) {
+  int done = 0;
+  for (const Profiler::Rec& r : g_prof.pending) {
+    if (hipEventQuery(r.b) != hipSuccess) break;  // launches complete in stream order
+    ++done;
+  }
+  if (total) *total = (int)g_prof.pending.size();
+  return done;
+}
+
 void upipe_profile_reset(void) {
   for (Profiler::Rec& r : g_prof.pending) {
     (void)hipEventDestroy(r.a);
