@@ -236,6 +236,7 @@ def main():
     ap.add_argument("--workload", default="llama8b_share_s1m")
     ap.add_argument("--head-chunk", type=int, default=None, help="default: the workload's smallest")
     ap.add_argument("--sweep", action="store_true", help="also run every head_chunk of the workload")
+    ap.add_argument("--sweep-chunks", default=None, help="comma-separated head_chunk values for --sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prefix", type=int, default=32768, help="positions in the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -275,7 +276,8 @@ def main():
           flush=True)
     sweep = []
     if args.sweep:
-        for h in w.head_chunks:
+        chunks = [int(x) for x in args.sweep_chunks.split(",")] if args.sweep_chunks else list(w.head_chunks)
+        for h in chunks:
             r = res if h == hc else run_one(w, h, args.steps, args.warmup, dev)[0]
             sweep.append({k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items()
                           if k_ != "kernels"})
