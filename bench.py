@@ -132,20 +132,7 @@ def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
         up.upipe_attn_bwd(q, k, v, out, out_lo, do, lse, dq, dk, dv, head_chunk, w.causal, ws, stream)
 
     def wait_reporting(what):
-        """Block until the enqueued work is done, printing a line each time one
-        of the library's attention kernels finishes (long multi-million-token
-        calls run for minutes)."""
-        seen, last = 0, time.perf_counter()
-        while True:
-            done, total = up.upipe_profile_completed()
-            now = time.perf_counter()
-            if done > seen and (done == total or now - last > 10.0):
-                print(f"[bench] {what}: {done}/{total} kernels finished", file=sys.stderr, flush=True)
-                seen, last = done, now
-            if done == total:
-                break
-            time.sleep(0.002)
-        torch.cuda.synchronize(dev)
+        up.wait_reporting(what, dev, prefix="[bench]")
 
     for _ in range(warmup):
         up.upipe_profile_reset()

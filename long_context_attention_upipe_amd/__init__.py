@@ -65,3 +65,28 @@ def attention_backward(q, k, v, out, dout, lse, out_lo=None, head_chunk=1, causa
         ws = workspace(S, Hq, Hkv, d, head_chunk, q.dtype, q.device, "bwd")
     upipe_attn_bwd(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, ws, stream)
     return dq, dk, dv
+
+
+def wait_reporting(what, device=None, interval=10.0, prefix="[upipe]"):
+    """Block until enqueued work is done, printing a line (to stderr) as the
+    library's kernels finish, at most every ``interval`` seconds.
+
+    Kernels are counted only while profiling is on (``upipe_profile_enable``);
+    with it off this is a plain device synchronize. Multi-million-token calls
+    run for minutes, and the line shows they are progressing."""
+    import sys
+    import time
+
+    import torch
+
+    seen, last = 0, time.perf_counter()
+    while True:
+        done, total = upipe_profile_completed()
+        now = time.perf_counter()
+        if done > seen and (done == total or now - last > interval):
+            print(f"{prefix} {what}: {done}/{total} kernels finished", file=sys.stderr, flush=True)
+            seen, last = done, now
+        if done == total:
+            break
+        time.sleep(0.002)
+    torch.cuda.synchronize(device)
