@@ -138,6 +138,20 @@ def _require(ts, dt):
             raise UpipeError(-1, f"dtype mismatch: {t.dtype} vs {dt}")
 
 
+def _require_shapes(q, named):
+    """The library sees plain pointers, so every buffer's extent is checked
+    here: a wrong shape would otherwise become an out-of-bounds access."""
+    S, Hq, d = q.shape
+    dev = q.device
+    for name, t, shape in named:
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(shape):
+            raise UpipeError(-1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.device != dev:
+            raise UpipeError(-1, f"{name} is on {t.device}, q on {dev}")
+
+
 def upipe_attn_fwd(q, k, v, out, out_lo, lse, head_chunk, causal, workspace, stream=None) -> None:
     """Enqueue the forward on ``stream`` (default: torch's current stream).
     ``out_lo`` (bf16, like ``out``, or None) receives out's rounding residual."""
@@ -145,9 +159,13 @@ def upipe_attn_fwd(q, k, v, out, out_lo, lse, head_chunk, causal, workspace, str
     _require((q, k, v, out) + ((out_lo,) if out_lo is not None else ()), q.dtype)
     _require((lse,), torch.float32)
     _require((workspace,), torch.uint8)
-    _check(lib().upipe_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(lse), S, Hq, Hkv, d,
-                                int(head_chunk), int(causal), dtype_code(q.dtype),
-                                _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+    _require_shapes(q, [("k", k, (S, Hkv, d)), ("v", v, (S, Hkv, d)), ("out", out, (S, Hq, d)),
+                        ("out_lo", out_lo, (S, Hq, d)), ("lse", lse, (Hq, S)),
+                        ("workspace", workspace, (workspace.numel(),))])
+    with torch.cuda.device(q.device):
+        _check(lib().upipe_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(lse), S, Hq, Hkv, d,
+                                    int(head_chunk), int(causal), dtype_code(q.dtype),
+                                    _ptr(workspace), workspace.numel(), _stream_handle(stream)))
 
 
 def upipe_attn_bwd(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, workspace, stream=None) -> None:
@@ -156,10 +174,15 @@ def upipe_attn_bwd(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, caus
     _require((q, k, v, out, dout, dq, dk, dv) + ((out_lo,) if out_lo is not None else ()), q.dtype)
     _require((lse,), torch.float32)
     _require((workspace,), torch.uint8)
-    _check(lib().upipe_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(dout), _ptr(lse),
-                                _ptr(dq), _ptr(dk), _ptr(dv), S, Hq, Hkv, d,
-                                int(head_chunk), int(causal), dtype_code(q.dtype),
-                                _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+    qs, ks = (S, Hq, d), (S, Hkv, d)
+    _require_shapes(q, [("k", k, ks), ("v", v, ks), ("out", out, qs), ("out_lo", out_lo, qs), ("dout", dout, qs),
+                        ("lse", lse, (Hq, S)), ("dq", dq, qs), ("dk", dk, ks), ("dv", dv, ks),
+                        ("workspace", workspace, (workspace.numel(),))])
+    with torch.cuda.device(q.device):
+        _check(lib().upipe_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(dout), _ptr(lse),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), S, Hq, Hkv, d,
+                                    int(head_chunk), int(causal), dtype_code(q.dtype),
+                                    _ptr(workspace), workspace.numel(), _stream_handle(stream)))
 
 
 def upipe_profile_enable(on: bool) -> None:

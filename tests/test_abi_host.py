@@ -146,3 +146,25 @@ def test_plan_rejects_small_table():
     arrs = [(ctypes.c_int32 * 1)() for _ in range(4)]
     assert L.lib().upipe_attn_plan(n, 1, 1, 1, *arrs) == -1
     assert "max_chunks" in L.upipe_last_error()
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("v", {"v": (64, 2, 32)}),
+    ("out", {"out": (64, 4, 32)}),
+    ("lse", {"lse": (64, 4)}),
+    ("dk", {"dk": (64, 1, 64)}),
+])
+def test_binding_rejects_mismatched_shapes(name, bad):
+    """The C ABI takes plain pointers; the binding checks every extent first."""
+    import torch
+
+    S, Hq, Hkv, d = 64, 4, 2, 64
+    shapes = {"k": (S, Hkv, d), "v": (S, Hkv, d), "out": (S, Hq, d), "lse": (Hq, S), "dk": (S, Hkv, d)}
+    shapes.update(bad)
+    q = torch.empty(S, Hq, d)
+    named = [(n, torch.empty(shp), exp) for n, shp, exp in [
+        ("k", shapes["k"], (S, Hkv, d)), ("v", shapes["v"], (S, Hkv, d)), ("out", shapes["out"], (S, Hq, d)),
+        ("lse", shapes["lse"], (Hq, S)), ("dk", shapes["dk"], (S, Hkv, d))]]
+    with pytest.raises(L.UpipeError, match=f"{name} has shape"):
+        L._require_shapes(q, named)
+    L._require_shapes(q, [(n, torch.empty(exp), exp) for n, _, exp in named])

@@ -155,3 +155,23 @@ def test_peaked_rows_accurate_with_residual():
     torch.cuda.synchronize()
     from gpu_util import errors
     print(f"    without residual: dq rel_fro={errors(f64(dq0), rdq)[1]:.3e}", flush=True)
+
+
+def test_wrong_shapes_raise_before_launch():
+    """Mis-shaped buffers are refused by the binding; nothing is enqueued and
+    a correct call afterwards still matches the oracle."""
+    dev = _dev()
+    w = custom(200, 2, 1, 64, "bf16", seed=5)
+    print(f"\n  case wrong shapes S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d}", flush=True)
+    q, k, v, do = make_inputs(w, device="cpu")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    ws = up.workspace(w.S, w.Hq, w.Hkv, w.d, 1, qd.dtype, dev, "both")
+    out = torch.empty_like(qd)
+    with pytest.raises(up.UpipeError, match="lse has shape"):
+        up.upipe_attn_fwd(qd, kd, vd, out, None, torch.empty(w.Hq, w.S - 1, device=dev), 1, 1, ws)
+    with pytest.raises(up.UpipeError, match="v has shape"):
+        up.upipe_attn_fwd(qd, kd, vd[:-1].contiguous(), out, None, torch.empty(w.Hq, w.S, device=dev), 1, 1, ws)
+    torch.cuda.synchronize()
+    r = run(qd, kd, vd, None, 1)
+    ro, rl = attention_forward(f64(q), f64(k), f64(v))
+    assert_close("out", f64(r["out"]), ro, w.dtype)
