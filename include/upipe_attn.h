@@ -45,6 +45,8 @@
  *     failed kernel launch returns UPIPE_EHIP.
  *   - Determinism: results are bit-identical across head_chunk values and
  *     across repeated calls (fixed key-tile order, no floating-point atomics).
+ *   - Outputs (out, out_lo, lse, dq, dk, dv) and the workspace must not
+ *     overlap each other or any input.
  *   - Calls that share a workspace must not overlap in time.
  */
 #ifndef UPIPE_ATTN_H
@@ -145,8 +147,9 @@ int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks,
  * itself. upipe_profile_read() waits for the recorded events, adds their
  * elapsed times into per-kernel totals, and copies up to max_kernels entries:
  * names[i] (static strings), launches[i], total_ms[i]. Returns the number of
- * kernel kinds seen since the last reset (host only; not thread-safe against
- * concurrent launches). upipe_profile_reset() drops all totals and events.
+ * kernel kinds seen since the last reset (host only; the totals are shared by
+ * all threads and guarded by a lock). upipe_profile_reset() drops all totals
+ * and events.
  */
 int upipe_profile_enable(int on);
 int upipe_profile_read(int max_kernels, const char** names, int64_t* launches, double* total_ms);

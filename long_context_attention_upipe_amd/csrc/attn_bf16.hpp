@@ -366,10 +366,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
         mma32(dp, tile_row_frag<D>(sO[cur], col, 2 * ks + half), tile_row_frag<D>(sV, wave * 32 + col, 2 * ks + half));
       }
       const bool need_mask = (p.causal && r0 < wkey0 + 31) || (r0 + BQ > S);
-      // row of register j = r0 + 4half + kj(j); it counts iff lo <= kj(j) <= hi
-      const int rb = r0 + half * 4;
-      const int lo = need_mask && p.causal ? my_key - rb : 0;
-      const int hi = need_mask ? S - 1 - rb : 31;
+      if (need_mask) {
+        // row of register j = r0 + 4half + kj(j); it counts iff lo <= kj(j) <= hi.
+        // Excluded scores become -inf, so their exp2 below is exactly 0.
+        const int rb = r0 + half * 4;
+        const int lo = p.causal ? my_key - rb : 0;
+        const int hi = S - 1 - rb;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kj = c_row(j, 0);
+          if (kj < lo || kj > hi) s[j] = -__builtin_inff();
+        }
+      }
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         const floatx4 l4 = *reinterpret_cast<const floatx4*>(&sLD[cur][jg * 8 + half * 4]);
@@ -377,9 +385,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = jg * 4 + e;
-          const int kj = c_row(j, 0);
-          const float pe = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l4[e]));
-          const float pij = (kj >= lo && kj <= hi) ? pe : 0.f;
+          const float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l4[e]));
           s[j] = pij;
           dp[j] = pij * (dp[j] - d4[e]);
         }

@@ -15,6 +15,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -156,7 +158,7 @@ enum KernelId { K_PACK = 0, K_UNPACK, K_FWD, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_
 const char* const kKernelNames[K_COUNT] = {"pack_heads", "unpack_heads", "attn_fwd", "bwd_pre", "attn_bwd_dkdv",
                                            "attn_bwd_dq"};
 struct Profiler {
-  bool on = false;
+  std::atomic<bool> on{false};
   struct Rec {
     int id;
     hipEvent_t a, b;
@@ -166,6 +168,7 @@ struct Profiler {
   double ms[K_COUNT] = {};
 };
 Profiler g_prof;
+std::mutex g_prof_mu;  // guards g_prof: launches and profile calls may come from several threads
 
 // Launch `fn` on stream `st`, bracketed by events when profiling is on.
 template <typename Fn>
@@ -189,6 +192,7 @@ void timed(int id, hipStream_t st, Fn&& fn) {
   fn();
   const bool ok_b = hipEventRecord(r.b, st) == hipSuccess;
   if (ok_a && ok_b) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
     g_prof.pending.push_back(r);
   } else {
     (void)hipEventDestroy(r.a);
@@ -196,6 +200,7 @@ void timed(int id, hipStream_t st, Fn&& fn) {
   }
 }
 
+// Caller holds g_prof_mu.
 int profile_flush() {
   for (Profiler::Rec& r : g_prof.pending) {
     hipError_t e = hipEventSynchronize(r.b);
@@ -411,6 +416,7 @@ int upipe_attn_fwd(const void* q, const void* k, const void* v, void* out, void*
   if (workspace_bytes < need)
     return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
   g_error.clear();
+  (void)hipGetLastError();  // launch errors are checked after each chunk; drop any older one first
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == UPIPE_BF16) {
@@ -439,6 +445,7 @@ int upipe_attn_bwd(const void* q, const void* k, const void* v, const void* out,
   if (workspace_bytes < need)
     return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
   g_error.clear();
+  (void)hipGetLastError();  // launch errors are checked after each chunk; drop any older one first
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (dtype == UPIPE_BF16) {
@@ -467,11 +474,13 @@ int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks, int32_t* q_
 }
 
 int upipe_profile_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
   g_prof.on = on != 0;
   return UPIPE_OK;
 }
 
 int upipe_profile_read(int max_kernels, const char** names, int64_t* launches, double* total_ms) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
   if (int rc = profile_flush()) return rc;
   int n = 0;
   for (int i = 0; i < K_COUNT; ++i) {
@@ -487,6 +496,7 @@ int upipe_profile_read(int max_kernels, const char** names, int64_t* launches, d
 }
 
 int upipe_profile_completed(int* total) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
   int done = 0;
   for (const Profiler::Rec& r : g_prof.pending) {
     if (hipEventQuery(r.b) != hipSuccess) break;  // launches complete in stream order
@@ -497,6 +507,7 @@ int upipe_profile_completed(int* total) {
 }
 
 void upipe_profile_reset(void) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
   for (Profiler::Rec& r : g_prof.pending) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
