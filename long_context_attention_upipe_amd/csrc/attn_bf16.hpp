@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
     df[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(dO + (size_t)my_row * D + ks * 16 + half * 8) : bf16x8{};
   }
   const float l2 = row_ok ? p.lse2[(size_t)hl * S + my_row] : 0.f;
-  const float Dr = row_ok ? p.Drow[(size_t)hl * S + my_row] : 0.f;
+  const float nD = row_ok ? p.negD[(size_t)hl * S + my_row] : 0.f;
 
   floatx16 acc[NDB];
 #pragma unroll
@@ -232,13 +232,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const float pij = c_row(j, 0) <= lim ? __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2)) : 0.f;
-            s[j] = pij * (dp[j] - Dr);  // dS^T
+            s[j] = pij * (dp[j] + nD);  // dS^T
           }
         } else {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2));
-            s[j] = pij * (dp[j] - Dr);  // dS^T
+            s[j] = pij * (dp[j] + nD);  // dS^T
           }
         }
 #pragma unroll
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
   constexpr int BKV = 128, BQ = 32, NKS = D / 16, NDB = D / 32;
   __shared__ __attribute__((aligned(1024))) bf16 sQ[2][BQ * D];
   __shared__ __attribute__((aligned(1024))) bf16 sO[2][BQ * D];  // dO rows
-  __shared__ __attribute__((aligned(256))) float sLD[2][2 * BQ];  // lse*log2(e) | D
+  __shared__ __attribute__((aligned(256))) float sLD[2][2 * BQ];  // lse*log2(e) | -D
   __shared__ __attribute__((aligned(1024))) bf16 sV[BKV * D];     // this workgroup's V rows
 
   const int tid = threadIdx.x;
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
     tile_load_async<D, BQ, 4>(sO[buf], p.dout + (size_t)hl * head_elems, r0, S, wave, lane);
     if (wave == 0) {
       const int r = min(r0 + (lane & 31), S - 1);
-      const float* src = (lane < 32 ? p.lse2 : p.Drow) + (size_t)hl * S + r;
+      const float* src = (lane < 32 ? p.lse2 : p.negD) + (size_t)hl * S + r;
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&sLD[buf][0], 4, 0, 0);
     }
   };
@@ -359,7 +359,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
     const int r0 = (qb0 + step % steps_per_head) * BQ;
     const bool active = (wkey0 < S) && !(p.causal && r0 + BQ - 1 < wkey0);
     if (active) {
-      floatx16 s = floatx16{}, dp = floatx16{};
+      // dP starts from -D of each row (register j: row r0 + 4half + kj(j)), so
+      // the MFMAs produce dP - D directly.
+      floatx16 s = floatx16{}, dp;
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(&sLD[cur][BQ + jg * 8 + half * 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[jg * 4 + e] = d4[e];
+      }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         mma32(s, tile_row_frag<D>(sQ[cur], col, 2 * ks + half), kf[ks]);
@@ -381,13 +389,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
         const floatx4 l4 = *reinterpret_cast<const floatx4*>(&sLD[cur][jg * 8 + half * 4]);
-        const floatx4 d4 = *reinterpret_cast<const floatx4*>(&sLD[cur][BQ + jg * 8 + half * 4]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = jg * 4 + e;
           const float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l4[e]));
           s[j] = pij;
-          dp[j] = pij * (dp[j] - d4[e]);
+          dp[j] = pij * dp[j];  // dS = P (dP - D)
         }
       }
 #pragma unroll

@@ -27,7 +27,7 @@ struct BwdParams {
   const T* v;          // pool: [nkv][S][D]
   const T* dout;       // pool: [hc][S][D]
   const float* lse;    // caller lse rows of the chunk's first head, [hc][S]
-  const float* Drow;   // pool: D = <dO, O> per row, [hc][S]
+  const float* negD;   // pool: -D = -<dO, O> per row, [hc][S]
   const float* lse2;   // pool: lse * log2(e) per row, [hc][S]
   T* dq;               // pool: [hc][S][D]
   float* dk_acc;       // pool: fp32 partial dK over earlier chunks, [nkv][S][D] (or null)
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdParams<T> p) {
     df[ks] = row_ok ? load_frag(dO + (size_t)my_row * D + ks * 16 + half * 8) : F{};
   }
   const float lse2 = row_ok ? p.lse[(size_t)hl * S + my_row] * kLog2e : 0.f;
-  const float Dr = row_ok ? p.Drow[(size_t)hl * S + my_row] : 0.f;
+  const float nD = row_ok ? p.negD[(size_t)hl * S + my_row] : 0.f;
 
   const int last_row = min(S, row0 + BQ) - 1;
   const int n_kt = p.causal ? (last_row / BK + 1) : ((S + BK - 1) / BK);
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdParams<T> p) {
           const int key = key0 + b * 32 + c_row(j, half);
           if ((p.causal && key > my_row) || key >= S) pij = 0.f;
         }
-        s[b][j] = pij * (dp[b][j] - Dr);  // dS^T
+        s[b][j] = pij * (dp[b][j] + nD);  // dS^T
       }
 
 #pragma unroll
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdParams<T> p) {
   __shared__ __attribute__((aligned(16))) T sO[BQ * RLD];   // dO rows
   __shared__ __attribute__((aligned(16))) T sOT[D * TLD];   // dO transposed
   __shared__ __attribute__((aligned(16))) float sL[BQ];     // lse * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[BQ];     // D
+  __shared__ __attribute__((aligned(16))) float sD[BQ];     // -D
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdParams<T> p) {
     if (tid < BQ) {
       const bool ok = r0 + tid < S;
       lreg = ok ? p.lse[(size_t)hl * S + r0 + tid] * kLog2e : 0.f;
-      dreg = ok ? p.Drow[(size_t)hl * S + r0 + tid] : 0.f;
+      dreg = ok ? p.negD[(size_t)hl * S + r0 + tid] : 0.f;
     }
   };
   auto store_block = [&]() {
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdParams<T> p) {
           if ((p.causal && my_key > row) || row >= S) pij = 0.f;
         }
         s[j] = pij;                     // P
-        dp[j] = pij * (dp[j] - d4[e]);  // dS
+        dp[j] = pij * (dp[j] + d4[e]);  // dS
       }
     }
 

@@ -7,8 +7,9 @@
 //    ("Road to 5 Million Tokens" talk summary, Chapters: Ulysses exchanges
 //    activations between GPUs; batched heads reuse the previous batch's
 //    buffer).
-//  * bwd_pre: D_i = <dO_i, O_i> per row in fp32 from the stored output (plus
-//    its stored rounding residual when there is one), the
+//  * bwd_pre: -D_i = -<dO_i, O_i> per row in fp32 from the stored output
+//    (plus its stored rounding residual when there is one; stored negated so
+//    the dK/dV kernel can start its dP accumulator from it), the
 //    chunk's dO rows packed, and lse_i * log2(e) (the base-2 exponent offset
 //    the backward kernels use), all in one pass.
 #pragma once
@@ -49,7 +50,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out, const T* __restrict__ out_lo,
                                                      const T* __restrict__ dout,
                                                      const float* __restrict__ lse, T* __restrict__ dout_pool,
-                                                     float* __restrict__ Drow, float* __restrict__ lse2, int S,
+                                                     float* __restrict__ negD, float* __restrict__ lse2, int S,
                                                      int H, int h0, int nh) {
   constexpr int EPV = 16 / sizeof(T);
   constexpr int TPR = D / EPV;  // lanes per row: 16 (bf16, d=128), 8, 16 or 32
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (sub == 0) {
-      Drow[(size_t)hl * S + i] = acc;
+      negD[(size_t)hl * S + i] = -acc;
       lse2[(size_t)hl * S + i] = lse[(size_t)(h0 + hl) * S + i] * kLog2e;
     }
   }

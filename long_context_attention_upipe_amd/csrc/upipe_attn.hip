@@ -127,7 +127,7 @@ FwdPool fwd_pool(const Problem& pr) {
 }
 
 struct BwdPool {
-  size_t q, dout, dq, k, v, drow, lse2, dk_acc, dv_acc, total;
+  size_t q, dout, dq, k, v, neg_d, lse2, dk_acc, dv_acc, total;
   bool has_acc;
 };
 BwdPool bwd_pool(const Problem& pr) {
@@ -139,7 +139,7 @@ BwdPool bwd_pool(const Problem& pr) {
   p.dq = off; off += align_up(pr.hc * U);
   p.k = off; off += align_up(pr.nkv * U);
   p.v = off; off += align_up(pr.nkv * U);
-  p.drow = off; off += align_up((size_t)pr.hc * pr.S * 4);
+  p.neg_d = off; off += align_up((size_t)pr.hc * pr.S * 4);
   p.lse2 = off; off += align_up((size_t)pr.hc * pr.S * 4);
   p.has_acc = pr.hc < pr.G;
   const size_t A = (size_t)pr.S * pr.d * 4;
@@ -299,7 +299,7 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
   T* dQc = reinterpret_cast<T*>(ws + pool.dq);
   T* Kc = reinterpret_cast<T*>(ws + pool.k);
   T* Vc = reinterpret_cast<T*>(ws + pool.v);
-  float* Dc = reinterpret_cast<float*>(ws + pool.drow);
+  float* nDc = reinterpret_cast<float*>(ws + pool.neg_d);
   float* L2c = reinterpret_cast<float*>(ws + pool.lse2);
   float* dKa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dk_acc) : nullptr;
   float* dVa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dv_acc) : nullptr;
@@ -329,7 +329,7 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
         (unsigned)std::min<size_t>((rows + kRowsPerPreBlock - 1) / kRowsPerPreBlock, 256 * 32);
     timed(K_BWD_PRE, st, [&] {
       hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st, (const T*)out, (const T*)out_lo, (const T*)dout, lse,
-                         dOc, Dc, L2c, S, pr.Hq, c.q_head0, pr.hc);
+                         dOc, nDc, L2c, S, pr.Hq, c.q_head0, pr.hc);
     });
 
     BwdParams<T> bp;
@@ -338,7 +338,7 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     bp.v = Vc;
     bp.dout = dOc;
     bp.lse = lse + (size_t)c.q_head0 * S;
-    bp.Drow = Dc;
+    bp.negD = nDc;
     bp.lse2 = L2c;
     bp.dq = dQc;
     bp.dk_acc = dKa;
