@@ -219,7 +219,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
       const bool need_mask = (p.causal && key0 + BK - 1 > wrow0) || (key0 + BK > S);
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        floatx16 s = floatx16{}, dp = floatx16{};
+        // dP starts from this lane's row -D, so the MFMAs yield dP - D
+        floatx16 s = floatx16{}, dp;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dp[j] = nD;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           mma32(s, tile_row_frag<D>(sK[cur], b * 32 + col, 2 * ks + half), qf[ks]);
@@ -232,13 +235,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const float pij = c_row(j, 0) <= lim ? __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2)) : 0.f;
-            s[j] = pij * (dp[j] + nD);  // dS^T
+            s[j] = pij * dp[j];  // dS^T = P (dP - D)
           }
         } else {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2));
-            s[j] = pij * (dp[j] + nD);  // dS^T
+            s[j] = pij * dp[j];  // dS^T = P (dP - D)
           }
         }
 #pragma unroll
