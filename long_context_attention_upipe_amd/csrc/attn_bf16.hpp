@@ -280,6 +280,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf16> p) {
   constexpr int BKV = 128, BQ = 32, NKS = D / 16, NDB = D / 32;
+  // These tiles use the layout with both read kinds conflict-free (kSwzAll):
+  // this kernel issues the most LDS reads per MFMA.
   __shared__ __attribute__((aligned(1024))) bf16 sQ[2][BQ * D];
   __shared__ __attribute__((aligned(1024))) bf16 sO[2][BQ * D];  // dO rows
   __shared__ __attribute__((aligned(256))) float sLD[2][2 * BQ];  // lse*log2(e) | -D
@@ -312,8 +314,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
     const int qb = qb0 + step % steps_per_head;
     const int hl = g * p.heads_per_kv + hi;
     const int r0 = qb * BQ;
-    tile_load_async<D, BQ, 4>(sQ[buf], p.q + (size_t)hl * head_elems, r0, S, wave, lane);
-    tile_load_async<D, BQ, 4>(sO[buf], p.dout + (size_t)hl * head_elems, r0, S, wave, lane);
+    tile_load_async<D, BQ, 4, kSwzAll>(sQ[buf], p.q + (size_t)hl * head_elems, r0, S, wave, lane);
+    tile_load_async<D, BQ, 4, kSwzAll>(sO[buf], p.dout + (size_t)hl * head_elems, r0, S, wave, lane);
     if (wave == 0) {
       const int r = min(r0 + (lane & 31), S - 1);
       const float* src = (lane < 32 ? p.lse2 : p.negD) + (size_t)hl * S + r;
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
 
   // V^T operand of dP = dO V^T stays in LDS (read per step); K^T stays in
   // registers: both together would not fit two waves per SIMD.
-  tile_load_async<D, BKV, 4>(sV, V, key0, S, wave, lane);
+  tile_load_async<D, BKV, 4, kSwzAll>(sV, V, key0, S, wave, lane);
   issue(0, 0);
 
   bf16x8 kf[NKS];
@@ -373,8 +375,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
       }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        mma32(s, tile_row_frag<D>(sQ[cur], col, 2 * ks + half), kf[ks]);
-        mma32(dp, tile_row_frag<D>(sO[cur], col, 2 * ks + half), tile_row_frag<D>(sV, wave * 32 + col, 2 * ks + half));
+        mma32(s, tile_row_frag<D, kSwzAll>(sQ[cur], col, 2 * ks + half), kf[ks]);
+        mma32(dp, tile_row_frag<D, kSwzAll>(sO[cur], col, 2 * ks + half), tile_row_frag<D, kSwzAll>(sV, wave * 32 + col, 2 * ks + half));
       }
       const bool need_mask = (p.causal && r0 < wkey0 + 31) || (r0 + BQ > S);
       if (need_mask) {
@@ -412,8 +414,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
         const bf16x8 dsf = to_frag(d8, bf16());
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          mma32(dv[db], tile_tr_frag<D>(sO[cur], st * 16, db * 32, lane), pf);
-          mma32(dk[db], tile_tr_frag<D>(sQ[cur], st * 16, db * 32, lane), dsf);
+          mma32(dv[db], tile_tr_frag<D, kSwzAll>(sO[cur], st * 16, db * 32, lane), pf);
+          mma32(dk[db], tile_tr_frag<D, kSwzAll>(sQ[cur], st * 16, db * 32, lane), dsf);
         }
       }
     }

@@ -14,23 +14,50 @@ typedef short short8v __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Chunk c (16 bytes = 8 bf16) of row r lives at chunk position c ^ swz(r).
-// swz takes distinct values mod 8 over any 8 consecutive rows (row-fragment
-// reads: 8 lanes, 8 rows, one chunk each) and distinct values of swz >> 1
-// over each aligned group of 4 rows (transposed reads: 4 rows x 2 adjacent
-// chunks per 16 lanes), so both read patterns spread over the banks.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Chunk c (16 bytes = 8 bf16) of row r lives at chunk position c ^ swz<D, M>(r).
+// LDS has 64 four-byte banks (256 bytes per pass): a 16-byte-per-lane read is
+// served 16 lanes at a time, an 8-byte-per-lane read 32 lanes at a time.
+//  * Row-fragment reads (ds_read_b128): 16 lanes read one chunk of 16
+//    consecutive rows; conflict-free when those 16 slots land on 16 different
+//    16-byte bank groups.
+//  * Transposed reads (ds_read_b64_tr_b16): 32 lanes read 4 consecutive chunks
+//    (4-aligned) of an aligned group of 4 rows, then the same 4 rows + 8.
+// Two layouts, chosen per kernel (each kernel fills and reads its own tiles):
+//  * kSwzTr: transposed reads conflict-free, row reads 2-way; swz has period 8
+//    in r, so the row+8 half of a transposed read is the first half's address
+//    plus an immediate offset.
+//  * kSwzAll: both read kinds conflict-free; swz has period 16, so the row+8
+//    half needs an address of its own.
+// d = 128 rows (256 bytes) span all banks; d = 64 rows (128 bytes) span half,
+// the row's parity picking the half.
+enum SwizzleMode { kSwzTr = 0, kSwzAll = 1 };
+
+template <int D, int M>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "tiles are 64 or 128 elements wide");
+  if constexpr (D == 128) {
+    // low 2 bits of r pick the top 2 bits: distinct across each aligned group of 4 rows
+    if constexpr (M == kSwzAll) return ((r & 3) << 2) | ((r >> 2) & 3);
+    return ((r & 3) << 2) | ((r >> 2) & 1);
+  } else {
+    if constexpr (M == kSwzAll) {
+      const int s = r >> 1;
+      return ((s & 1) << 2) | ((s >> 1) & 3);
+    }
+    return ((r & 3) << 1) | ((r >> 2) & 1);
+  }
+}
 
 // Element offset of chunk `chunk` of row `row` in a tile with D-element rows.
-template <int D>
+template <int D, int M = kSwzTr>
 __device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * D + ((chunk ^ swz(row)) << 3);
+  return row * D + ((chunk ^ swz<D, M>(row)) << 3);
 }
 
 // Row fragment: elements [8*chunk, 8*chunk + 8) of `row`.
-template <int D>
+template <int D, int M = kSwzTr>
 __device__ __forceinline__ bf16x8 tile_row_frag(const bf16* tile, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(tile + tile_off<D>(row, chunk));
+  return *reinterpret_cast<const bf16x8*>(tile + tile_off<D, M>(row, chunk));
 }
 
 // Transposed fragment for an MFMA A/B operand whose contraction runs over the
@@ -41,15 +68,15 @@ __device__ __forceinline__ bf16x8 tile_row_frag(const bf16* tile, int row, int c
 // ds_read_b64_tr_b16 gathers 4 rows: within a 16-lane group, lane i gets
 // element i & 3 of the 8-byte slot addressed by lane (i >> 2) + 4k as its
 // k-th value, so lane j addresses row 4*half + (j >> 2), columns 4*(j & 3)..+3.
-template <int D>
+template <int D, int M = kSwzTr>
 __device__ __forceinline__ bf16x8 tile_tr_frag(const bf16* tile, int rbase, int col0, int lane) {
   const int g = lane >> 4, j = lane & 15;
   const int half = g >> 1, m0 = (g & 1) << 4;
   const int row = rbase + (half << 2) + (j >> 2);
   const int col = col0 + m0 + ((j & 3) << 2);
   const int chunk = col >> 3, sub = col & 7;
-  const bf16* p0 = tile + row * D + ((chunk ^ swz(row)) << 3) + sub;
-  const bf16* p1 = tile + (row + 8) * D + ((chunk ^ swz(row + 8)) << 3) + sub;
+  const bf16* p0 = tile + row * D + ((chunk ^ swz<D, M>(row)) << 3) + sub;
+  const bf16* p1 = tile + (row + 8) * D + ((chunk ^ swz<D, M>(row + 8)) << 3) + sub;
   const short4v a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p0);
   const short4v b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p1);
   const short8v c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -61,7 +88,7 @@ __device__ __forceinline__ bf16x8 tile_tr_frag(const bf16* tile, int rbase, int 
 // instruction fills 1 KiB of LDS, 16 bytes per lane, lane order; the lane
 // picks the global chunk that belongs at its LDS position. Asynchronous:
 // complete with wait_vm() and a barrier before reading.
-template <int D, int ROWS, int NWAVES>
+template <int D, int ROWS, int NWAVES, int M = kSwzTr>
 __device__ __forceinline__ void tile_load_async(bf16* tile, const bf16* g, int g_row0, int S, int wave, int lane) {
   constexpr int CPR = D / 8;
   constexpr int SLOTS = ROWS * CPR;
@@ -73,7 +100,7 @@ __device__ __forceinline__ void tile_load_async(bf16* tile, const bf16* g, int g
     const int i = k * NWAVES + wave;
     const int slot = i * 64 + lane;
     const int r = slot / CPR, pos = slot % CPR;
-    const int c = pos ^ swz(r);
+    const int c = pos ^ swz<D, M>(r);
     const int gr = min(g_row0 + r, S - 1);
     __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)gr * D + c * 8), (lds_void*)(tile + i * 512), 16, 0,
                                      0);
