@@ -223,11 +223,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
         floatx16 s = floatx16{}, dp;
 #pragma unroll
         for (int j = 0; j < 16; ++j) dp[j] = nD;
+        // MFMA runs at raised wave priority, so the SIMD's other wave (in
+        // its softmax) does not delay the MFMA issue stream.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           mma32(s, tile_row_frag<D>(sK[cur], b * 32 + col, 2 * ks + half), qf[ks]);
           mma32(dp, tile_row_frag<D>(sV[cur], b * 32 + col, 2 * ks + half), df[ks]);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (need_mask) {
           // key of register j = key0 + 32b + 4half + kj(j); keep it iff kj(j) <= lim
           const int kb = key0 + b * 32 + half * 4;
@@ -244,6 +248,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
             s[j] = pij * dp[j];  // dS^T = P (dP - D)
           }
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           floatx8 d8;
@@ -254,6 +259,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
           for (int db = 0; db < NDB; ++db)
             mma32(acc[db], tile_tr_frag<D>(sK[cur], b * 32 + st * 16, db * 32, lane), dsf);
         }
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     wait_vm();
@@ -373,11 +379,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
 #pragma unroll
         for (int e = 0; e < 4; ++e) dp[jg * 4 + e] = d4[e];
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         mma32(s, tile_row_frag<D, kSwzAll>(sQ[cur], col, 2 * ks + half), kf[ks]);
         mma32(dp, tile_row_frag<D, kSwzAll>(sO[cur], col, 2 * ks + half), tile_row_frag<D, kSwzAll>(sV, wave * 32 + col, 2 * ks + half));
       }
+      __builtin_amdgcn_s_setprio(0);
       const bool need_mask = (p.causal && r0 < wkey0 + 31) || (r0 + BQ > S);
       if (need_mask) {
         // row of register j = r0 + 4half + kj(j); it counts iff lo <= kj(j) <= hi.
@@ -402,6 +410,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
           dp[j] = pij * dp[j];  // dS = P (dP - D)
         }
       }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         floatx8 p8, d8;
@@ -418,6 +427,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
           mma32(dk[db], tile_tr_frag<D, kSwzAll>(sQ[cur], st * 16, db * 32, lane), dsf);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     wait_vm();
     __syncthreads();
