@@ -281,7 +281,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV: 4 waves x 32 keys; query rows in steps of 32 (head-major, ascending).
+// dK/dV: 4 waves x 32 keys; query rows in steps of 32, head-major, each head's
+// row blocks from the last one down to the workgroup's diagonal. Workgroups
+// resident together then read the same Q/dO block at about the same time, so
+// it is fetched once per L2 instead of once per workgroup.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf16> p) {
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
 
   auto issue = [&](int step, int buf) {
     const int hi = step / steps_per_head;
-    const int qb = qb0 + step % steps_per_head;
+    const int qb = n_qb - 1 - step % steps_per_head;
     const int hl = g * p.heads_per_kv + hi;
     const int r0 = qb * BQ;
     tile_load_async<D, BQ, 4, kSwzAll>(sQ[buf], p.q + (size_t)hl * head_elems, r0, S, wave, lane);
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
   for (int step = 0; step < n_steps; ++step) {
     const int cur = step & 1;
     if (step + 1 < n_steps) issue(step + 1, cur ^ 1);
-    const int r0 = (qb0 + step % steps_per_head) * BQ;
+    const int r0 = (n_qb - 1 - step % steps_per_head) * BQ;
     const bool active = (wkey0 < S) && !(p.causal && r0 + BQ - 1 < wkey0);
     if (active) {
       // dP starts from -D of each row (register j: row r0 + 4half + kj(j)), so
