@@ -93,10 +93,18 @@ def cpu_baseline(w, q, k, v, do, s_prefix: int):
     attention_backward(*arrs, causal=w.causal)  # recomputes the forward inside
     dt = time.perf_counter() - t0
     flops = 14 * w.d * w.Hq * pairs(s_prefix, w.causal)
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return {
         "value": round(flops / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model,
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"fp64 numpy oracle, causal fwd+bwd of the first {s_prefix} positions of the same "
                   f"inputs (Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}), {dt:.1f} s",
