@@ -77,9 +77,18 @@ __host__ __device__ __forceinline__ int perm16(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Combine a value with the one held by lane ^ 32, without going through LDS:
+// v_permlane32_swap of x with itself returns {x[0..31], x[0..31]} and
+// {x[32..63], x[32..63]}, so every lane sees its own value and its partner's.
 __device__ __forceinline__ float wave_xor32_max(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float wave_xor32_sum(float x) { return x + __shfl_xor(x, 32); }
+__device__ __forceinline__ float wave_xor32_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace upipe
