@@ -318,9 +318,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
   const int steps_per_head = n_qb - qb0;
   const int n_steps = p.heads_per_kv * steps_per_head;
 
-  auto issue = [&](int step, int buf) {
-    const int hi = step / steps_per_head;
-    const int qb = n_qb - 1 - step % steps_per_head;
+  // Step order: head hi ascending, row block qb from n_qb - 1 down to qb0.
+  // (hi, qb) cursors advance by compare-and-select instead of dividing the
+  // step index each step.
+  auto advance = [&](int& hi, int& qb) {
+    if (qb == qb0) {
+      qb = n_qb - 1;
+      ++hi;
+    } else {
+      --qb;
+    }
+  };
+  auto issue = [&](int hi, int qb, int buf) {
     const int hl = g * p.heads_per_kv + hi;
     const int r0 = qb * BQ;
     tile_load_async<D, BQ, 4, kSwzAll>(sQ[buf], p.q + (size_t)hl * head_elems, r0, S, wave, lane);
@@ -335,7 +344,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
   // V^T operand of dP = dO V^T stays in LDS (read per step); K^T stays in
   // registers: both together would not fit two waves per SIMD.
   tile_load_async<D, BKV, 4, kSwzAll>(sV, V, key0, S, wave, lane);
-  issue(0, 0);
+  int next_hi = 0, next_qb = n_qb - 1;  // the next step to copy in
+  int cur_qb = n_qb - 1;                // the step being computed
+  int cur_hi = 0;
+  issue(next_hi, next_qb, 0);
+  advance(next_hi, next_qb);
 
   bf16x8 kf[NKS];
 #pragma unroll
@@ -369,8 +382,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
   __syncthreads();
   for (int step = 0; step < n_steps; ++step) {
     const int cur = step & 1;
-    if (step + 1 < n_steps) issue(step + 1, cur ^ 1);
-    const int r0 = (n_qb - 1 - step % steps_per_head) * BQ;
+    if (step + 1 < n_steps) {
+      issue(next_hi, next_qb, cur ^ 1);
+      advance(next_hi, next_qb);
+    }
+    const int r0 = cur_qb * BQ;
     const bool active = (wkey0 < S) && !(p.causal && r0 + BQ - 1 < wkey0);
     if (active) {
       // dP starts from -D of each row (register j: row r0 + 4half + kj(j)), so
@@ -432,6 +448,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
       }
       __builtin_amdgcn_s_setprio(0);
     }
+    advance(cur_hi, cur_qb);
     wait_vm();
     __syncthreads();
   }
