@@ -16,8 +16,10 @@ Sources (web pages, cited by title and section):
 [MAXTEXT] Article on long-context training in MaxText v0.2.4 on Cloud TPU:
         the release section (attention variants MHA / GQA / MLA; Splash skips
         fully masked blocks), the section on where long-sequence training gets
-        stuck (each position looks back over all earlier positions), and the
-        strategy-choice table (Ulysses splits heads, not positions).
+        stuck (each position looks back over all earlier positions), the
+        strategy-choice table (Ulysses splits heads, not positions), and the
+        note that several samples packed into one long sequence need no
+        padding under Splash attention.
 
 What the oracle computes. Under Ulysses-style context parallelism a GPU runs
 exact attention for its own heads over the whole sequence [ROAD Chapters,
@@ -28,6 +30,8 @@ approximated, so this module writes the definition of attention out, in
 float64, with every input taken as the exact value of its element:
 
     A(i)   = {0..i} if causal else {0..S-1}            (look-back set)
+             intersected, for packed sequences, with doc(i) = the positions
+             of the document that holds i [MAXTEXT, packing note]
     s_ij   = tau * <q_hi, k_gj>,  tau = 1/sqrt(d),  g = kv head of h
     LSE_hi = log sum_{j in A(i)} exp(s_ij)             (natural log)
     P_ij   = exp(s_ij - LSE_hi)
@@ -44,7 +48,11 @@ Readings where the pages are silent or ambiguous:
   * causal look-back includes the position itself (j <= i);
   * tau = 1/sqrt(d); LSE is a natural log;
   * GQA heads are grouped contiguously: q head h reads kv head h // (Hq/Hkv);
-  * layouts: q, k, v, dO, O are [S, H, d] (token-major); LSE is [Hq, S].
+  * layouts: q, k, v, dO, O are [S, H, d] (token-major); LSE is [Hq, S];
+  * packed documents are contiguous runs of positions given by offsets
+    0 = o_0 <= o_1 <= ... <= o_n = S (document m holds o_m .. o_{m+1}-1;
+    empty documents are allowed); a position attends only within its own
+    document, and causally within it when causal.
 
 Algorithm: row blocks of R query rows; for each block the full score rows are
 formed, then (1) the row max, (2) exp and row sum, (3) the weighted sum of V.
@@ -65,6 +73,7 @@ __all__ = [
     "forward_rows",
     "backward_rows_dq",
     "backward_cols_dkdv",
+    "document_bounds",
 ]
 
 # Upper bound on the number of float64 score elements held at once (512 MiB).
@@ -82,11 +91,31 @@ def kv_head_of(h: int, n_q_heads: int, n_kv_heads: int) -> int:
     return h // (n_q_heads // n_kv_heads)
 
 
-def _look_back_mask(rows: np.ndarray, n_cols: int, causal: bool) -> np.ndarray | None:
+def document_bounds(doc_offsets, S: int):
+    """(first, last): for every position i, the first and the last position of
+    the document that holds i, from offsets o_0 = 0 <= ... <= o_n = S."""
+    off = np.asarray(doc_offsets, dtype=np.int64)
+    if off.ndim != 1 or len(off) < 2 or off[0] != 0 or off[-1] != S or np.any(np.diff(off) < 0):
+        raise ValueError("document offsets must rise from 0 to S")
+    doc = np.searchsorted(off, np.arange(S), side="right") - 1  # last m with o_m <= i
+    return off[doc], off[doc + 1] - 1
+
+
+def _look_back_mask(rows: np.ndarray, n_cols: int, causal: bool, bounds=None) -> np.ndarray | None:
     """True where key j is NOT in A(i) for each row i in ``rows``."""
-    if not causal:
-        return None
-    return np.arange(n_cols)[None, :] > rows[:, None]
+    mask = None
+    if causal:
+        mask = np.arange(n_cols)[None, :] > rows[:, None]
+    if bounds is not None:
+        first, last = bounds
+        cols = np.arange(n_cols)[None, :]
+        outside = (cols < first[rows][:, None]) | (cols > last[rows][:, None])
+        mask = outside if mask is None else (mask | outside)
+    return mask
+
+
+def _bounds(doc_offsets, S):
+    return None if doc_offsets is None else document_bounds(doc_offsets, S)
 
 
 def _softmax_rows(s: np.ndarray):
@@ -98,12 +127,15 @@ def _softmax_rows(s: np.ndarray):
     return e / l, (m + np.log(l))[..., 0]
 
 
-def attention_forward(q, k, v, causal: bool = True, block: int = 256):
-    """Full-tensor forward. Returns (out [S,Hq,d], lse [Hq,S]) in float64."""
+def attention_forward(q, k, v, causal: bool = True, block: int = 256, doc_offsets=None):
+    """Full-tensor forward. Returns (out [S,Hq,d], lse [Hq,S]) in float64.
+
+    ``doc_offsets`` (optional) splits the sequence into packed documents."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     S, Hq, d = q.shape
     Hkv = k.shape[1]
     tau = 1.0 / math.sqrt(d)
+    bounds = _bounds(doc_offsets, S)
     out = np.zeros((S, Hq, d))
     lse = np.zeros((Hq, S))
     for h in range(Hq):
@@ -113,7 +145,7 @@ def attention_forward(q, k, v, causal: bool = True, block: int = 256):
             rows = np.arange(r0, r1)
             n_cols = r1 if causal else S
             s = tau * (q[r0:r1, h, :] @ k[:n_cols, g, :].T)
-            mask = _look_back_mask(rows, n_cols, causal)
+            mask = _look_back_mask(rows, n_cols, causal, bounds)
             if mask is not None:
                 s[mask] = -np.inf
             p, lse_blk = _softmax_rows(s)
@@ -122,7 +154,7 @@ def attention_forward(q, k, v, causal: bool = True, block: int = 256):
     return out, lse
 
 
-def attention_backward(q, k, v, dout, causal: bool = True, block: int = 256):
+def attention_backward(q, k, v, dout, causal: bool = True, block: int = 256, doc_offsets=None):
     """Full-tensor backward. Returns (dq, dk, dv) in float64, shaped like q, k, v.
 
     P is recomputed from the exact forward's LSE; D uses the exact O.
@@ -131,7 +163,8 @@ def attention_backward(q, k, v, dout, causal: bool = True, block: int = 256):
     S, Hq, d = q.shape
     Hkv = k.shape[1]
     tau = 1.0 / math.sqrt(d)
-    out, lse = attention_forward(q, k, v, causal, block)
+    bounds = _bounds(doc_offsets, S)
+    out, lse = attention_forward(q, k, v, causal, block, doc_offsets)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -144,7 +177,7 @@ def attention_backward(q, k, v, dout, causal: bool = True, block: int = 256):
             q_blk = q[r0:r1, h, :]
             do_blk = dout[r0:r1, h, :]
             s = tau * (q_blk @ k[:n_cols, g, :].T)
-            mask = _look_back_mask(rows, n_cols, causal)
+            mask = _look_back_mask(rows, n_cols, causal, bounds)
             if mask is not None:
                 s[mask] = -np.inf
             p = np.exp(s - lse[h, r0:r1][:, None])
@@ -192,7 +225,7 @@ def _rows_matmul(a, b):
     return (a.reshape(R * G, n) @ b).reshape(R, G, b.shape[1])
 
 
-def forward_rows(q_rows, k, v, rows, causal: bool = True):
+def forward_rows(q_rows, k, v, rows, causal: bool = True, doc_offsets=None):
     """Exact O and LSE at selected query rows, O(S*d) work per row.
 
     ``q_rows`` [R,Hq,d] holds the query vectors of positions ``rows``. The
@@ -205,12 +238,13 @@ def forward_rows(q_rows, k, v, rows, causal: bool = True):
     Hq = q_rows.shape[1]
     G = Hq // Hkv
     tau = 1.0 / math.sqrt(d)
+    bounds = _bounds(doc_offsets, S)
     out = np.zeros((len(rows), Hq, d))
     lse = np.zeros((Hq, len(rows)))
     for sel in _row_batches(rows, S, causal, G):
         r = rows[sel]
         n_cols = int(r.max()) + 1 if causal else S
-        mask = _look_back_mask(r, n_cols, causal)
+        mask = _look_back_mask(r, n_cols, causal, bounds)
         for g in range(Hkv):
             hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]
             s = _group_scores(q_rows[sel][:, hs, :], k[:n_cols, g, :], tau, mask)
@@ -220,7 +254,7 @@ def forward_rows(q_rows, k, v, rows, causal: bool = True):
     return out, lse
 
 
-def backward_rows_dq(q_rows, k, v, dout_rows, rows, causal: bool = True):
+def backward_rows_dq(q_rows, k, v, dout_rows, rows, causal: bool = True, doc_offsets=None):
     """Exact dQ at selected query rows, O(S*d) work per row.
 
     ``q_rows`` and ``dout_rows`` [R,Hq,d] hold q and dO at positions ``rows``.
@@ -233,11 +267,12 @@ def backward_rows_dq(q_rows, k, v, dout_rows, rows, causal: bool = True):
     Hq = q_rows.shape[1]
     G = Hq // Hkv
     tau = 1.0 / math.sqrt(d)
+    bounds = _bounds(doc_offsets, S)
     dq = np.zeros((len(rows), Hq, d))
     for sel in _row_batches(rows, S, causal, G):
         r = rows[sel]
         n_cols = int(r.max()) + 1 if causal else S
-        mask = _look_back_mask(r, n_cols, causal)
+        mask = _look_back_mask(r, n_cols, causal, bounds)
         for g in range(Hkv):
             hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]
             s = _group_scores(q_rows[sel][:, hs, :], k[:n_cols, g, :], tau, mask)
@@ -251,23 +286,30 @@ def backward_rows_dq(q_rows, k, v, dout_rows, rows, causal: bool = True):
     return dq
 
 
-def backward_cols_dkdv(q, k, v, dout, cols, causal: bool = True):
+def backward_cols_dkdv(q, k, v, dout, cols, causal: bool = True, doc_offsets=None):
     """Exact dK and dV at selected key rows, from the inputs alone.
 
     Key j collects from every row i with j in A(i): i >= j when causal, every
-    row otherwise. Each such row's LSE and O come from :func:`forward_rows`, so
-    the cost is O(|rows| * S * d), which is small when the keys lie near the
-    end of a causal sequence. Returns (dk_cols [C,Hkv,d], dv_cols [C,Hkv,d]).
+    row otherwise, and with packed documents only rows of j's own document.
+    Each such row's LSE and O come from :func:`forward_rows`, so the cost is
+    O(|rows| * S * d), which is small when the keys lie near the end of a
+    causal sequence or in short documents.
+    Returns (dk_cols [C,Hkv,d], dv_cols [C,Hkv,d]).
     """
     k, v = _f64(k), _f64(v)
     cols = np.asarray(cols, dtype=np.int64)
     S, Hkv, d = k.shape
     Hq = q.shape[1]
     tau = 1.0 / math.sqrt(d)
+    bounds = _bounds(doc_offsets, S)
     first = int(cols.min()) if causal else 0
-    need = np.arange(first, S)
-    q_need, do_need = _f64(q[first:]), _f64(dout[first:])
-    o_need, lse_need = forward_rows(q_need, k, v, need, causal)
+    end = S
+    if bounds is not None:
+        first = max(first, int(bounds[0][cols].min()))
+        end = int(bounds[1][cols].max()) + 1
+    need = np.arange(first, end)
+    q_need, do_need = _f64(q[first:end]), _f64(dout[first:end])
+    o_need, lse_need = forward_rows(q_need, k, v, need, causal, doc_offsets)
     dk = np.zeros((len(cols), Hkv, d))
     dv = np.zeros((len(cols), Hkv, d))
     n_rows = len(need)
@@ -276,6 +318,9 @@ def backward_cols_dkdv(q, k, v, dout, cols, causal: bool = True):
         cj = cols[c0:c0 + per]
         # row i (absolute index need[t]) contributes to key j only if j in A(i)
         excluded = (need[None, :] < cj[:, None]) if causal else None
+        if bounds is not None:
+            other_doc = (bounds[0][need][None, :] > cj[:, None]) | (bounds[1][need][None, :] < cj[:, None])
+            excluded = other_doc if excluded is None else (excluded | other_doc)
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             qh = q_need[:, h, :]

@@ -210,6 +210,124 @@ def pin_sampled_functions(mod, S=53, Hq=4, Hkv=1, d=8):
         np.testing.assert_allclose(dv_c, dv[cols], rtol=1e-11, atol=1e-12)
 
 
+# --- packed documents -------------------------------------------------------
+# Offsets with an empty document, a length-1 document, documents that end
+# mid-way and one that runs to the end.
+DOC_OFFSETS = [0, 1, 9, 9, 24, 30, 41]
+
+
+def _doc_allowed(S, offsets, causal):
+    """[S,S] booleans, True where row i may attend to key j: one square block
+    per document, lower triangle when causal."""
+    allowed = np.zeros((S, S), dtype=bool)
+    for a, b in zip(offsets[:-1], offsets[1:]):
+        allowed[a:b, a:b] = True
+    if causal:
+        allowed &= np.tril(np.ones((S, S), dtype=bool))
+    return allowed
+
+
+def pin_docs_sdpa(mod, S=41, Hq=4, Hkv=2, d=8):
+    """Packed documents against torch's fp64 SDPA (and its autograd) with an
+    explicit block-diagonal boolean mask."""
+    q, k, v = _rand((S, Hq, d), 41), _rand((S, Hkv, d), 42), _rand((S, Hkv, d), 43)
+    do = _rand((S, Hq, d), 44)
+    G = Hq // Hkv
+    for causal in (True, False):
+        mask = torch.tensor(_doc_allowed(S, DOC_OFFSETS, causal))
+        out, lse = mod.attention_forward(q, k, v, causal=causal, block=7, doc_offsets=DOC_OFFSETS)
+        dq, dk, dv = mod.attention_backward(q, k, v, do, causal=causal, block=7, doc_offsets=DOC_OFFSETS)
+        tq = torch.tensor(q, requires_grad=True)
+        tk = torch.tensor(k, requires_grad=True)
+        tv = torch.tensor(v, requires_grad=True)
+        qh = tq.permute(1, 0, 2).unsqueeze(0)
+        kh = tk.permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0)
+        vh = tv.permute(1, 0, 2).repeat_interleave(G, dim=0).unsqueeze(0)
+        o = F.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask).squeeze(0).permute(1, 0, 2)
+        np.testing.assert_allclose(out, o.detach().numpy(), rtol=1e-12, atol=1e-12)
+        sc = (qh[0] @ kh[0].transpose(1, 2)) / math.sqrt(d)
+        ref_lse = torch.logsumexp(sc.masked_fill(~mask, float("-inf")), dim=-1).detach().numpy()
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+        o.backward(torch.tensor(do))
+        np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def pin_docs_packed_equals_separate(mod, S=41, Hq=4, Hkv=1, d=8):
+    """Packing is invisible: each document's rows and keys come out as if that
+    document had been run alone (every output, causal and not)."""
+    q, k, v = _rand((S, Hq, d), 45), _rand((S, Hkv, d), 46), _rand((S, Hkv, d), 47)
+    do = _rand((S, Hq, d), 48)
+    for causal in (True, False):
+        out, lse = mod.attention_forward(q, k, v, causal=causal, block=6, doc_offsets=DOC_OFFSETS)
+        grads = mod.attention_backward(q, k, v, do, causal=causal, block=6, doc_offsets=DOC_OFFSETS)
+        for a, b in zip(DOC_OFFSETS[:-1], DOC_OFFSETS[1:]):
+            if a == b:
+                continue
+            o1, l1 = mod.attention_forward(q[a:b], k[a:b], v[a:b], causal=causal, block=6)
+            np.testing.assert_allclose(out[a:b], o1, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(lse[:, a:b], l1, rtol=1e-12, atol=1e-13)
+            g1 = mod.attention_backward(q[a:b], k[a:b], v[a:b], do[a:b], causal=causal, block=6)
+            for x, y in zip(grads, g1):
+                np.testing.assert_allclose(x[a:b], y, rtol=1e-11, atol=1e-12)
+
+
+def pin_docs_single_is_plain(mod, S=29, Hq=2, Hkv=1, d=8):
+    """One document spanning the sequence is the unpacked computation, exactly."""
+    q, k, v = _rand((S, Hq, d), 49), _rand((S, Hkv, d), 50), _rand((S, Hkv, d), 51)
+    do = _rand((S, Hq, d), 52)
+    for causal in (True, False):
+        a = mod.attention_forward(q, k, v, causal=causal, block=8, doc_offsets=[0, S])
+        b = mod.attention_forward(q, k, v, causal=causal, block=8)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+        a = mod.attention_backward(q, k, v, do, causal=causal, block=8, doc_offsets=[0, S])
+        b = mod.attention_backward(q, k, v, do, causal=causal, block=8)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+
+
+def pin_docs_length_one(mod, S=13, Hq=4, Hkv=2, d=8):
+    """Every document one position long: each row sees only itself, so
+    O_i = v_i, LSE_i = <q_i,k_i>/sqrt(d), dQ = dK = 0 (P = 1 leaves dS = 0) and
+    dV_j = the group's sum of dO_j."""
+    q, k, v = _rand((S, Hq, d), 53), _rand((S, Hkv, d), 54), _rand((S, Hkv, d), 55)
+    do = _rand((S, Hq, d), 56)
+    G = Hq // Hkv
+    offs = list(range(S + 1))
+    for causal in (True, False):
+        out, lse = mod.attention_forward(q, k, v, causal=causal, doc_offsets=offs)
+        dq, dk, dv = mod.attention_backward(q, k, v, do, causal=causal, doc_offsets=offs)
+        for h in range(Hq):
+            g = h // G
+            np.testing.assert_allclose(out[:, h, :], v[:, g, :], rtol=0, atol=1e-15)
+            np.testing.assert_allclose(lse[h], (q[:, h, :] * k[:, g, :]).sum(-1) / math.sqrt(d), rtol=1e-13)
+        np.testing.assert_allclose(dq, 0.0, atol=1e-14)
+        np.testing.assert_allclose(dk, 0.0, atol=1e-14)
+        np.testing.assert_allclose(dv, do.reshape(S, Hkv, G, d).sum(axis=2), rtol=1e-13, atol=1e-14)
+
+
+def pin_docs_sampled_functions(mod, S=41, Hq=4, Hkv=2, d=8):
+    """The per-row and per-key functions agree with the full-tensor ones under
+    packed documents."""
+    q, k, v = _rand((S, Hq, d), 57), _rand((S, Hkv, d), 58), _rand((S, Hkv, d), 59)
+    do = _rand((S, Hq, d), 60)
+    for causal in (True, False):
+        out, lse = mod.attention_forward(q, k, v, causal=causal, block=5, doc_offsets=DOC_OFFSETS)
+        dq, dk, dv = mod.attention_backward(q, k, v, do, causal=causal, block=5, doc_offsets=DOC_OFFSETS)
+        rows = np.array([0, 1, 8, 9, 23, 24, 29, 30, 40, 15])
+        o_r, l_r = mod.forward_rows(q[rows], k, v, rows, causal=causal, doc_offsets=DOC_OFFSETS)
+        np.testing.assert_allclose(o_r, out[rows], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(l_r, lse[:, rows], rtol=1e-12, atol=1e-13)
+        dq_r = mod.backward_rows_dq(q[rows], k, v, do[rows], rows, causal=causal, doc_offsets=DOC_OFFSETS)
+        np.testing.assert_allclose(dq_r, dq[rows], rtol=1e-11, atol=1e-12)
+        for cols in (np.array([40, 31, 25, 12]), np.array([0, 5]), np.array([29, 24])):
+            dk_c, dv_c = mod.backward_cols_dkdv(q, k, v, do, cols, causal=causal, doc_offsets=DOC_OFFSETS)
+            np.testing.assert_allclose(dk_c, dk[cols], rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(dv_c, dv[cols], rtol=1e-11, atol=1e-12)
+
+
 ALL_PINS = [
     pin_sdpa_forward,
     pin_sdpa_backward,
@@ -222,6 +340,11 @@ ALL_PINS = [
     pin_key_shift,
     pin_gqa_equals_repeated_mha,
     pin_sampled_functions,
+    pin_docs_sdpa,
+    pin_docs_packed_equals_separate,
+    pin_docs_single_is_plain,
+    pin_docs_length_one,
+    pin_docs_sampled_functions,
 ]
 
 

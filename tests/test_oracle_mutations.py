@@ -23,11 +23,22 @@ MUTATIONS = {
     "bwd_dq_transposed_k": ("dq[r0:r1, h, :] = tau * (ds @ k[:n_cols, g, :])", "dq[r0:r1, h, :] = tau * (ds @ v[:n_cols, g, :])"),
     "cols_wrong_causal_side": ("(need[None, :] < cj[:, None])", "(need[None, :] > cj[:, None])"),
     "cols_dv_missing": ("dv[c0:c0 + per, g, :] += p @ doh", "dv[c0:c0 + per, g, :] += 0 * (p @ doh)"),
-    "fwd_rows_noncausal_width": ("        n_cols = int(r.max()) + 1 if causal else S\n        mask = _look_back_mask(r, n_cols, causal)\n        for g in range(Hkv):\n            hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]\n            s = _group_scores(q_rows[sel][:, hs, :], k[:n_cols, g, :], tau, mask)\n            p, lse_blk",
-                                 "        n_cols = int(r.max()) + 1\n        mask = _look_back_mask(r, n_cols, causal)\n        for g in range(Hkv):\n            hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]\n            s = _group_scores(q_rows[sel][:, hs, :], k[:n_cols, g, :], tau, mask)\n            p, lse_blk"),
+    "fwd_rows_noncausal_width": ("        n_cols = int(r.max()) + 1 if causal else S\n        mask = _look_back_mask(r, n_cols, causal, bounds)\n        for g in range(Hkv):\n            hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]\n            s = _group_scores(q_rows[sel][:, hs, :], k[:n_cols, g, :], tau, mask)\n            p, lse_blk",
+                                 "        n_cols = int(r.max()) + 1\n        mask = _look_back_mask(r, n_cols, causal, bounds)\n        for g in range(Hkv):\n            hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]\n            s = _group_scores(q_rows[sel][:, hs, :], k[:n_cols, g, :], tau, mask)\n            p, lse_blk"),
     "rows_dq_missing_D": ("            ds = p * (dp - D[..., None])", "            ds = p * dp"),
     "group_scores_mask_ignored": ("        s[np.broadcast_to(mask[:, None, :], s.shape)] = -np.inf", "        pass"),
     "softmax_wrong_axis": ("    m = s.max(axis=-1, keepdims=True)", "    m = s.max(axis=0, keepdims=True)"),
+    "docs_last_off_by_one": ("return off[doc], off[doc + 1] - 1", "return off[doc], off[doc + 1]"),
+    "docs_search_left": ('doc = np.searchsorted(off, np.arange(S), side="right") - 1',
+                         'doc = np.searchsorted(off, np.arange(S), side="left") - 1'),
+    "docs_mask_no_lower": ("outside = (cols < first[rows][:, None]) | (cols > last[rows][:, None])",
+                           "outside = (cols > last[rows][:, None])"),
+    "docs_mask_no_upper": ("outside = (cols < first[rows][:, None]) | (cols > last[rows][:, None])",
+                           "outside = (cols < first[rows][:, None])"),
+    "docs_mask_replaces_causal": ("mask = outside if mask is None else (mask | outside)", "mask = outside"),
+    "cols_docs_ignored": ("excluded = other_doc if excluded is None else (excluded | other_doc)", "pass"),
+    "cols_docs_first_row": ("first = max(first, int(bounds[0][cols].min()))", "first = max(first, int(bounds[0][cols].max()))"),
+    "cols_docs_end_row": ("end = int(bounds[1][cols].max()) + 1", "end = int(bounds[1][cols].min()) + 1"),
 }
 
 
