@@ -70,8 +70,21 @@ def measured_traffic(kernel: str, workload: str, head_chunk: int):
     return None
 
 
-def pairs(S: int, causal: bool) -> int:
-    return S * (S + 1) // 2 if causal else S * S
+def pairs(S: int, causal: bool, offsets=None) -> int:
+    """Unmasked (row, key) pairs of one head: the causal triangle, the full
+    square, or their sum over packed documents."""
+    if offsets is None:
+        return S * (S + 1) // 2 if causal else S * S
+    lens = [int(b) - int(a) for a, b in zip(offsets[:-1], offsets[1:])]
+    return sum(n * (n + 1) // 2 if causal else n * n for n in lens)
+
+
+def prefix_offsets(offsets, n: int):
+    """Document offsets of the first n positions (None stays None)."""
+    if offsets is None:
+        return None
+    cut = [int(o) for o in offsets if int(o) < n]
+    return cut + [n]
 
 
 def cpu_baseline(w, q, k, v, do, s_prefix: int):
@@ -87,12 +100,15 @@ def cpu_baseline(w, q, k, v, do, s_prefix: int):
         threads = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) or 1
     except Exception:  # noqa: BLE001
         threads = os.cpu_count() or 1
+    from long_context_attention_upipe_amd.workloads import doc_offsets
+
     sl = slice(0, s_prefix)
     arrs = [t[sl].float().cpu().numpy().astype(np.float64) for t in (q, k, v, do)]
+    offs = prefix_offsets(doc_offsets(w), s_prefix)
     t0 = time.perf_counter()
-    attention_backward(*arrs, causal=w.causal)  # recomputes the forward inside
+    attention_backward(*arrs, causal=w.causal, doc_offsets=offs)  # recomputes the forward inside
     dt = time.perf_counter() - t0
-    flops = 14 * w.d * w.Hq * pairs(s_prefix, w.causal)
+    flops = 14 * w.d * w.Hq * pairs(s_prefix, w.causal, offs)
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -107,7 +123,8 @@ def cpu_baseline(w, q, k, v, do, s_prefix: int):
         "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"fp64 numpy oracle, causal fwd+bwd of the first {s_prefix} positions of the same "
-                  f"inputs (Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}), {dt:.1f} s",
+                  f"inputs (Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}"
+                  + (f", {len(offs) - 1} documents" if offs is not None else "") + f"), {dt:.1f} s",
         "seconds": round(dt, 3),
     }
 
@@ -116,7 +133,7 @@ def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
     import torch
 
     import long_context_attention_upipe_amd as up
-    from long_context_attention_upipe_amd.workloads import make_inputs
+    from long_context_attention_upipe_amd.workloads import doc_offsets, make_inputs
 
     torch.cuda.synchronize(dev)
     torch.cuda.empty_cache()
@@ -132,12 +149,25 @@ def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
                    up.upipe_attn_bwd_workspace_bytes(w.S, w.Hq, w.Hkv, w.d, head_chunk, code))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    offsets = doc_offsets(w)
 
-    def fwd():
-        up.upipe_attn_fwd(q, k, v, out, out_lo, lse, head_chunk, w.causal, ws, stream)
+    if offsets is None:
+        def fwd():
+            up.upipe_attn_fwd(q, k, v, out, out_lo, lse, head_chunk, w.causal, ws, stream)
 
-    def bwd():
-        up.upipe_attn_bwd(q, k, v, out, out_lo, do, lse, dq, dk, dv, head_chunk, w.causal, ws, stream)
+        def bwd():
+            up.upipe_attn_bwd(q, k, v, out, out_lo, do, lse, dq, dk, dv, head_chunk, w.causal, ws, stream)
+    else:
+        offs_t = torch.from_numpy(offsets).to(dev)
+        up._lib._require_docs(q, offs_t)  # values checked once, outside the timed region
+
+        def fwd():
+            up.upipe_attn_fwd_docs(q, k, v, out, out_lo, lse, head_chunk, w.causal, offs_t, ws, stream,
+                                   check_offsets=False)
+
+        def bwd():
+            up.upipe_attn_bwd_docs(q, k, v, out, out_lo, do, lse, dq, dk, dv, head_chunk, w.causal, offs_t, ws, stream,
+                                   check_offsets=False)
 
     def wait_reporting(what):
         up.wait_reporting(what, dev, prefix="[bench]")
@@ -173,7 +203,7 @@ def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     ms_per_step = (t1 - t0) * 1000.0 / steps
-    P = pairs(w.S, w.causal)
+    P = pairs(w.S, w.causal, offsets)
     f_fwd = 4 * w.d * w.Hq * P
     f_bwd = 10 * w.d * w.Hq * P
     peak_alloc = torch.cuda.max_memory_allocated(dev) - base
@@ -219,7 +249,9 @@ def roofline(w, res, head_chunk):
         "frac": round(achieved / peak, 4),
         "traffic": measured_traffic(name, w.name, head_chunk),
         "per_unit": f"{ALGO_FLOPS_PER_PAIR_D[name]}*d FLOP per unmasked (row, key) pair and head; "
-                    f"{head_chunk} heads x S(S+1)/2 pairs per launch",
+                    f"{head_chunk} heads x "
+                    + ("S(S+1)/2" if not w.doc_lengths else "the sum over documents of L(L+1)/2")
+                    + " pairs per launch",
     }
 
 
@@ -286,6 +318,13 @@ def main():
         print(f"[bench] cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads", file=sys.stderr,
               flush=True)
 
+    config = {"workload": w.name, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "head_chunk": hc,
+              "causal": w.causal, "parallelism": "1 GPU's Ulysses head share, UPipe head chunks"}
+    if w.doc_lengths:
+        from long_context_attention_upipe_amd.workloads import doc_offsets
+
+        config["documents"] = len(doc_offsets(w)) - 1
+        config["doc_lengths_loguniform"] = list(w.doc_lengths)
     line = {
         "metric": METRIC,
         "value": round(res["tflops"], 3),
@@ -299,8 +338,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) q/k/v, dO ~ N(0,1)/sqrt(S), drawn on device)",
-        "config": {"workload": w.name, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "head_chunk": hc,
-                   "causal": w.causal, "parallelism": "1 GPU's Ulysses head share, UPipe head chunks"},
+        "config": config,
         "pct_bf16_peak": round(100.0 * res["tflops"] / PEAK_BF16_TFLOPS, 2),
         "fwd_ms": round(res["fwd_ms"], 3),
         "bwd_ms": round(res["bwd_ms"], 3),

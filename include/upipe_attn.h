@@ -127,6 +127,45 @@ int upipe_attn_bwd(const void* q, const void* k, const void* v,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Packed documents (MaxText long-context article: several samples packed into
+ * one long sequence need no padding, and blocks that the mask excludes
+ * entirely are skipped). The same forward and backward as above, where a
+ * position attends only to positions of its own document -- and, when causal,
+ * only to itself and earlier positions of it:
+ *   A(i) = { j : doc(j) == doc(i) and (j <= i or causal == 0) }
+ * replaces the look-back set in every formula above.
+ *
+ * doc_offsets: DEVICE pointer to n_docs + 1 int32 values
+ *   0 = o_0 <= o_1 <= ... <= o_{n_docs} = S, 4-byte aligned; document m holds
+ *   positions o_m .. o_{m+1} - 1 (empty documents are allowed). Owned by the
+ *   caller and only read, by the kernels, in stream order.
+ * n_docs >= 1. One document [0, S] gives results bit-identical to
+ *   upipe_attn_fwd / upipe_attn_bwd.
+ * Key tiles outside a query tile's documents are never loaded or computed.
+ * Errors: a NULL doc_offsets or n_docs < 1 fails as UPIPE_EINVAL before
+ *   anything is enqueued. The offsets themselves live on the device and are
+ *   not checked: offsets that break the rules above give unspecified results,
+ *   but every access still stays inside the caller's tensors and the pool.
+ * Workspace: the same sizes as upipe_attn_fwd / upipe_attn_bwd. The backward
+ *   must get the same doc_offsets as the forward that produced out and lse.
+ */
+int upipe_attn_fwd_docs(const void* q, const void* k, const void* v,
+                        void* out, void* out_lo, float* lse,
+                        int64_t S, int Hq, int Hkv, int d, int head_chunk,
+                        int causal, const int32_t* doc_offsets, int n_docs,
+                        int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+int upipe_attn_bwd_docs(const void* q, const void* k, const void* v,
+                        const void* out, const void* out_lo, const void* dout,
+                        const float* lse,
+                        void* dq, void* dk, void* dv,
+                        int64_t S, int Hq, int Hkv, int d, int head_chunk,
+                        int causal, const int32_t* doc_offsets, int n_docs,
+                        int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The head-chunk plan, for inspection (host only, no device work). Fills up to
  * max_chunks entries; entry c describes chunk c:
  *   q_head0[c]  first query head of the chunk (it covers head_chunk heads)

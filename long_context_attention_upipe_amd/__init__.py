@@ -11,8 +11,10 @@ from ._lib import (  # noqa: F401
     UpipeError,
     dtype_code,
     upipe_attn_bwd,
+    upipe_attn_bwd_docs,
     upipe_attn_bwd_workspace_bytes,
     upipe_attn_fwd,
+    upipe_attn_fwd_docs,
     upipe_attn_fwd_workspace_bytes,
     upipe_attn_plan,
     upipe_last_error,
@@ -36,11 +38,13 @@ def workspace(S, Hq, Hkv, d, head_chunk, dtype, device="cuda", which="both"):
     return torch.empty(max(sizes), dtype=torch.uint8, device=device)
 
 
-def attention_forward(q, k, v, head_chunk=1, causal=True, ws=None, stream=None, residual=True):
+def attention_forward(q, k, v, head_chunk=1, causal=True, ws=None, stream=None, residual=True, doc_offsets=None):
     """(out, lse, out_lo) of attention over [S,Hq,d] / [S,Hkv,d] device tensors.
 
     out_lo is out's bf16 rounding residual (None for fp32 or residual=False);
-    pass it to attention_backward for an accurate D = <dout, out>."""
+    pass it to attention_backward for an accurate D = <dout, out>.
+    doc_offsets (int32 [n_docs + 1] on the device, 0 .. S) packs documents:
+    each position then attends only within its own document."""
     import torch
 
     S, Hq, d = q.shape
@@ -50,12 +54,17 @@ def attention_forward(q, k, v, head_chunk=1, causal=True, ws=None, stream=None, 
     lse = torch.empty((Hq, S), dtype=torch.float32, device=q.device)
     if ws is None:
         ws = workspace(S, Hq, Hkv, d, head_chunk, q.dtype, q.device, "fwd")
-    upipe_attn_fwd(q, k, v, out, out_lo, lse, head_chunk, causal, ws, stream)
+    if doc_offsets is None:
+        upipe_attn_fwd(q, k, v, out, out_lo, lse, head_chunk, causal, ws, stream)
+    else:
+        upipe_attn_fwd_docs(q, k, v, out, out_lo, lse, head_chunk, causal, doc_offsets, ws, stream)
     return out, lse, out_lo
 
 
-def attention_backward(q, k, v, out, dout, lse, out_lo=None, head_chunk=1, causal=True, ws=None, stream=None):
-    """dq, dk, dv of attention given the forward's out, lse (and out_lo)."""
+def attention_backward(q, k, v, out, dout, lse, out_lo=None, head_chunk=1, causal=True, ws=None, stream=None,
+                       doc_offsets=None):
+    """dq, dk, dv of attention given the forward's out, lse (and out_lo), and
+    the forward's doc_offsets if it had them."""
     import torch
 
     S, Hq, d = q.shape
@@ -63,7 +72,11 @@ def attention_backward(q, k, v, out, dout, lse, out_lo=None, head_chunk=1, causa
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if ws is None:
         ws = workspace(S, Hq, Hkv, d, head_chunk, q.dtype, q.device, "bwd")
-    upipe_attn_bwd(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, ws, stream)
+    if doc_offsets is None:
+        upipe_attn_bwd(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, ws, stream)
+    else:
+        upipe_attn_bwd_docs(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, doc_offsets, ws,
+                            stream)
     return dq, dk, dv
 
 

@@ -51,6 +51,16 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz,
                                  vp]
     L.upipe_attn_bwd.restype = i32
+    # The packed-document entry points are bound when the loaded build has
+    # them (UPIPE_ATTN_LIBRARY may name an older build); calling them on a
+    # build without them raises AttributeError.
+    if hasattr(L, "upipe_attn_fwd_docs"):
+        L.upipe_attn_fwd_docs.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp, i32, i32, vp,
+                                          sz, vp]
+        L.upipe_attn_fwd_docs.restype = i32
+        L.upipe_attn_bwd_docs.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp,
+                                          i32, i32, vp, sz, vp]
+        L.upipe_attn_bwd_docs.restype = i32
     p32 = ctypes.POINTER(ctypes.c_int32)
     L.upipe_attn_plan.argtypes = [i32, i32, i32, i32, p32, p32, p32, p32]
     L.upipe_attn_plan.restype = i32
@@ -183,6 +193,65 @@ def upipe_attn_bwd(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, caus
                                     _ptr(dq), _ptr(dk), _ptr(dv), S, Hq, Hkv, d,
                                     int(head_chunk), int(causal), dtype_code(q.dtype),
                                     _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+
+
+def _require_docs(q, doc_offsets, check_values=True) -> int:
+    """Checks the packed-document offsets (int32 [n_docs + 1] on q's device,
+    rising from 0 to S) and returns n_docs. The library reads them on the
+    device only, so their values are checked here (one device sync; a caller
+    that has checked them once may pass check_values=False)."""
+    S = q.shape[0]
+    t = doc_offsets
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+        raise UpipeError(-1, "doc_offsets must be a contiguous 1-D int32 tensor")
+    if t.device != q.device:
+        raise UpipeError(-1, f"doc_offsets is on {t.device}, q on {q.device}")
+    if t.numel() < 2:
+        raise UpipeError(-1, "doc_offsets needs at least two entries (0 and S)")
+    if not check_values:
+        return t.numel() - 1
+    ok = (t[0] == 0) & (t[-1] == S) & (t[1:] >= t[:-1]).all()
+    if not bool(ok.item()):
+        raise UpipeError(-1, f"doc_offsets must rise (non-strictly) from 0 to S={S}")
+    return t.numel() - 1
+
+
+def upipe_attn_fwd_docs(q, k, v, out, out_lo, lse, head_chunk, causal, doc_offsets, workspace, stream=None,
+                        check_offsets=True) -> None:
+    """Forward over packed documents (``doc_offsets``: int32 [n_docs + 1] on the device)."""
+    S, Hq, Hkv, d = _shape(q, k)
+    _require((q, k, v, out) + ((out_lo,) if out_lo is not None else ()), q.dtype)
+    _require((lse,), torch.float32)
+    _require((workspace,), torch.uint8)
+    _require_shapes(q, [("k", k, (S, Hkv, d)), ("v", v, (S, Hkv, d)), ("out", out, (S, Hq, d)),
+                        ("out_lo", out_lo, (S, Hq, d)), ("lse", lse, (Hq, S)),
+                        ("workspace", workspace, (workspace.numel(),))])
+    n_docs = _require_docs(q, doc_offsets, check_offsets)
+    with torch.cuda.device(q.device):
+        _check(lib().upipe_attn_fwd_docs(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(lse), S, Hq, Hkv,
+                                         d, int(head_chunk), int(causal), _ptr(doc_offsets), n_docs,
+                                         dtype_code(q.dtype), _ptr(workspace), workspace.numel(),
+                                         _stream_handle(stream)))
+
+
+def upipe_attn_bwd_docs(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, doc_offsets, workspace,
+                        stream=None, check_offsets=True) -> None:
+    """Backward over packed documents (the same ``doc_offsets`` as the forward)."""
+    S, Hq, Hkv, d = _shape(q, k)
+    _require((q, k, v, out, dout, dq, dk, dv) + ((out_lo,) if out_lo is not None else ()), q.dtype)
+    _require((lse,), torch.float32)
+    _require((workspace,), torch.uint8)
+    qs, ks = (S, Hq, d), (S, Hkv, d)
+    _require_shapes(q, [("k", k, ks), ("v", v, ks), ("out", out, qs), ("out_lo", out_lo, qs), ("dout", dout, qs),
+                        ("lse", lse, (Hq, S)), ("dq", dq, qs), ("dk", dk, ks), ("dv", dv, ks),
+                        ("workspace", workspace, (workspace.numel(),))])
+    n_docs = _require_docs(q, doc_offsets, check_offsets)
+    with torch.cuda.device(q.device):
+        _check(lib().upipe_attn_bwd_docs(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(dout), _ptr(lse),
+                                         _ptr(dq), _ptr(dk), _ptr(dv), S, Hq, Hkv, d,
+                                         int(head_chunk), int(causal), _ptr(doc_offsets), n_docs,
+                                         dtype_code(q.dtype), _ptr(workspace), workspace.numel(),
+                                         _stream_handle(stream)))
 
 
 def upipe_profile_enable(on: bool) -> None:

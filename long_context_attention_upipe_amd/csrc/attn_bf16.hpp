@@ -45,11 +45,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
   const int wrow0 = row0 + wave * 32;
   const int my_row = wrow0 + col;
 
+  // Keys this lane's row attends to, [kw.first, kw.last]; both bounds grow
+  // with the row, so lanes 0 and 31 give the wave's extremes and the
+  // workgroup's first and last rows its key-tile range.
   const int last_row = min(S, row0 + BQ) - 1;
-  const int n_kt = p.causal ? (last_row / BK + 1) : ((S + BK - 1) / BK);
+  const DocSpan kw = key_window(p.doc_off, p.n_docs, min(my_row, S - 1), S, p.causal);
+  const int w_first_min = __builtin_amdgcn_readlane(kw.first, 0);
+  const int w_first_max = __builtin_amdgcn_readlane(kw.first, 31);
+  const int w_last_min = __builtin_amdgcn_readlane(kw.last, 0);
+  const int w_last_max = __builtin_amdgcn_readlane(kw.last, 31);
+  const int kt_begin = p.doc_off ? key_window(p.doc_off, p.n_docs, row0, S, p.causal).first / BK : 0;
+  const int kt_end = key_window(p.doc_off, p.n_docs, last_row, S, p.causal).last / BK + 1;
 
-  tile_load_async<D, BK, 4>(sK[0], K, 0, S, wave, lane);
-  tile_load_async<D, BK, 4>(sV[0], V, 0, S, wave, lane);
+  tile_load_async<D, BK, 4>(sK[kt_begin & 1], K, kt_begin * BK, S, wave, lane);
+  tile_load_async<D, BK, 4>(sV[kt_begin & 1], V, kt_begin * BK, S, wave, lane);
 
   bf16x8 qf[NKS];
 #pragma unroll
@@ -65,14 +74,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
 
   wait_vm();
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < n_kt) {
+    if (kt + 1 < kt_end) {
       tile_load_async<D, BK, 4>(sK[cur ^ 1], K, (kt + 1) * BK, S, wave, lane);
       tile_load_async<D, BK, 4>(sV[cur ^ 1], V, (kt + 1) * BK, S, wave, lane);
     }
     const int key0 = kt * BK;
-    const bool active = (wrow0 < S) && (!p.causal || key0 <= wrow0 + 31);
+    const bool active = (wrow0 < S) && key0 + BK - 1 >= w_first_min && key0 <= w_last_max;
     if (active) {
       floatx16 s[2];
 #pragma unroll
@@ -81,16 +90,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) mma32(s[b], tile_row_frag<D>(sK[cur], b * 32 + col, 2 * ks + half), qf[ks]);
       }
-      const bool need_mask = (p.causal && key0 + BK - 1 > wrow0) || (key0 + BK > S);
+      const bool need_mask = key0 < w_first_max || key0 + BK - 1 > w_last_min;
       if (need_mask) {
-        // key of register j = key0 + 32b + 4half + kj(j); keep it iff kj(j) <= lim
+        // key of register j = key0 + 32b + 4half + kj(j); keep it iff lo <= kj(j) <= hi
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const int kb = key0 + b * 32 + half * 4;
-          const int lim = p.causal ? min(my_row - kb, S - 1 - kb) : S - 1 - kb;
+          const int lo = kw.first - kb, hi = kw.last - kb;
 #pragma unroll
           for (int j = 0; j < 16; ++j)
-            if (c_row(j, 0) > lim) s[b][j] = NEG_INF;
+            if (c_row(j, 0) < lo || c_row(j, 0) > hi) s[b][j] = NEG_INF;
         }
       }
       float mx = NEG_INF;
@@ -186,11 +195,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
   const int my_row = wrow0 + col;
   const bool row_ok = my_row < S;
 
+  // Key windows as in the forward kernel.
   const int last_row = min(S, row0 + BQ) - 1;
-  const int n_kt = p.causal ? (last_row / BK + 1) : ((S + BK - 1) / BK);
+  const DocSpan kw = key_window(p.doc_off, p.n_docs, min(my_row, S - 1), S, p.causal);
+  const int w_first_min = __builtin_amdgcn_readlane(kw.first, 0);
+  const int w_first_max = __builtin_amdgcn_readlane(kw.first, 31);
+  const int w_last_min = __builtin_amdgcn_readlane(kw.last, 0);
+  const int w_last_max = __builtin_amdgcn_readlane(kw.last, 31);
+  const int kt_begin = p.doc_off ? key_window(p.doc_off, p.n_docs, row0, S, p.causal).first / BK : 0;
+  const int kt_end = key_window(p.doc_off, p.n_docs, last_row, S, p.causal).last / BK + 1;
 
-  tile_load_async<D, BK, 4>(sK[0], K, 0, S, wave, lane);
-  tile_load_async<D, BK, 4>(sV[0], V, 0, S, wave, lane);
+  tile_load_async<D, BK, 4>(sK[kt_begin & 1], K, kt_begin * BK, S, wave, lane);
+  tile_load_async<D, BK, 4>(sV[kt_begin & 1], V, kt_begin * BK, S, wave, lane);
 
   bf16x8 qf[NKS], df[NKS];
 #pragma unroll
@@ -207,16 +223,16 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
 
   wait_vm();
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < n_kt) {
+    if (kt + 1 < kt_end) {
       tile_load_async<D, BK, 4>(sK[cur ^ 1], K, (kt + 1) * BK, S, wave, lane);
       tile_load_async<D, BK, 4>(sV[cur ^ 1], V, (kt + 1) * BK, S, wave, lane);
     }
     const int key0 = kt * BK;
-    const bool active = (wrow0 < S) && (!p.causal || key0 <= wrow0 + 31);
+    const bool active = (wrow0 < S) && key0 + BK - 1 >= w_first_min && key0 <= w_last_max;
     if (active) {
-      const bool need_mask = (p.causal && key0 + BK - 1 > wrow0) || (key0 + BK > S);
+      const bool need_mask = key0 < w_first_max || key0 + BK - 1 > w_last_min;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         // dP starts from this lane's row -D, so the MFMAs yield dP - D
@@ -233,12 +249,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
         }
         __builtin_amdgcn_s_setprio(0);
         if (need_mask) {
-          // key of register j = key0 + 32b + 4half + kj(j); keep it iff kj(j) <= lim
+          // key of register j = key0 + 32b + 4half + kj(j); keep it iff lo <= kj(j) <= hi
           const int kb = key0 + b * 32 + half * 4;
-          const int lim = p.causal ? min(my_row - kb, S - 1 - kb) : S - 1 - kb;
+          const int lo = kw.first - kb, hi = kw.last - kb;
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const float pij = c_row(j, 0) <= lim ? __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2)) : 0.f;
+            const int kj = c_row(j, 0);
+            const float pij = (kj >= lo && kj <= hi) ? __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2)) : 0.f;
             s[j] = pij * dp[j];  // dS^T = P (dP - D)
           }
         } else {
@@ -313,17 +330,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
   const int my_key = wkey0 + col;
   const bool key_ok = my_key < S;
 
-  const int n_qb = (S + BQ - 1) / BQ;
-  const int qb0 = p.causal ? key0 / BQ : 0;
-  const int steps_per_head = n_qb - qb0;
+  // Query rows that attend to this lane's key, [rw.first, rw.last]; both
+  // bounds grow with the key, so lanes 0 and 31 give the wave's extremes and
+  // the workgroup's first and last keys its row-block range [qb0, qb_top].
+  const int last_key = min(S, key0 + BKV) - 1;
+  DocSpan rw = row_window(p.doc_off, p.n_docs, min(my_key, S - 1), S, p.causal);
+  if (p.causal) rw.first = my_key;  // a key past the end has no rows
+  const int w_first_min = __builtin_amdgcn_readlane(rw.first, 0);
+  const int w_first_max = __builtin_amdgcn_readlane(rw.first, 31);
+  const int w_last_min = __builtin_amdgcn_readlane(rw.last, 0);
+  const int w_last_max = __builtin_amdgcn_readlane(rw.last, 31);
+  const int qb0 = row_window(p.doc_off, p.n_docs, key0, S, p.causal).first / BQ;
+  const int qb_top = row_window(p.doc_off, p.n_docs, last_key, S, p.causal).last / BQ;
+  const int steps_per_head = qb_top - qb0 + 1;
   const int n_steps = p.heads_per_kv * steps_per_head;
 
-  // Step order: head hi ascending, row block qb from n_qb - 1 down to qb0.
+  // Step order: head hi ascending, row block qb from qb_top down to qb0.
   // (hi, qb) cursors advance by compare-and-select instead of dividing the
   // step index each step.
   auto advance = [&](int& hi, int& qb) {
     if (qb == qb0) {
-      qb = n_qb - 1;
+      qb = qb_top;
       ++hi;
     } else {
       --qb;
@@ -344,8 +371,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
   // V^T operand of dP = dO V^T stays in LDS (read per step); K^T stays in
   // registers: both together would not fit two waves per SIMD.
   tile_load_async<D, BKV, 4, kSwzAll>(sV, V, key0, S, wave, lane);
-  int next_hi = 0, next_qb = n_qb - 1;  // the next step to copy in
-  int cur_qb = n_qb - 1;                // the step being computed
+  int next_hi = 0, next_qb = qb_top;  // the next step to copy in
+  int cur_qb = qb_top;                // the step being computed
   int cur_hi = 0;
   issue(next_hi, next_qb, 0);
   advance(next_hi, next_qb);
@@ -387,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
       advance(next_hi, next_qb);
     }
     const int r0 = cur_qb * BQ;
-    const bool active = (wkey0 < S) && !(p.causal && r0 + BQ - 1 < wkey0);
+    const bool active = (wkey0 < S) && r0 + BQ - 1 >= w_first_min && r0 <= w_last_max;
     if (active) {
       // dP starts from -D of each row (register j: row r0 + 4half + kj(j)), so
       // the MFMAs produce dP - D directly.
@@ -405,13 +432,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
         mma32(dp, tile_row_frag<D, kSwzAll>(sO[cur], col, 2 * ks + half), tile_row_frag<D, kSwzAll>(sV, wave * 32 + col, 2 * ks + half));
       }
       __builtin_amdgcn_s_setprio(0);
-      const bool need_mask = (p.causal && r0 < wkey0 + 31) || (r0 + BQ > S);
+      const bool need_mask = r0 < w_first_max || r0 + BQ - 1 > w_last_min;
       if (need_mask) {
         // row of register j = r0 + 4half + kj(j); it counts iff lo <= kj(j) <= hi.
         // Excluded scores become -inf, so their exp2 below is exactly 0.
         const int rb = r0 + half * 4;
-        const int lo = p.causal ? my_key - rb : 0;
-        const int hi = S - 1 - rb;
+        const int lo = rw.first - rb;
+        const int hi = rw.last - rb;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int kj = c_row(j, 0);

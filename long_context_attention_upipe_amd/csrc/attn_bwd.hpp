@@ -42,6 +42,8 @@ struct BwdParams {
   int n_qtiles;        // ceil(S / 128) (dQ kernel)
   int n_ktiles;        // ceil(S / 128) (dK/dV kernel)
   int causal;
+  const int* doc_off;  // packed-document offsets o_0..o_n (device), or null
+  int n_docs;          // n
   int acc_load;        // dK/dV start from dk_acc/dv_acc instead of zero
   int finalize;        // write tau*dK, dV as T to dk_out/dv_out (else fp32 to the acc)
   float scale;         // tau
@@ -108,8 +110,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdParams<T> p) {
   const float lse2 = row_ok ? p.lse[(size_t)hl * S + my_row] * kLog2e : 0.f;
   const float nD = row_ok ? p.negD[(size_t)hl * S + my_row] : 0.f;
 
+  // Key windows as in the forward kernel.
   const int last_row = min(S, row0 + BQ) - 1;
-  const int n_kt = p.causal ? (last_row / BK + 1) : ((S + BK - 1) / BK);
+  const DocSpan kw = key_window(p.doc_off, p.n_docs, min(my_row, S - 1), S, p.causal);
+  const int w_first_min = __builtin_amdgcn_readlane(kw.first, 0);
+  const int w_first_max = __builtin_amdgcn_readlane(kw.first, 31);
+  const int w_last_min = __builtin_amdgcn_readlane(kw.last, 0);
+  const int w_last_max = __builtin_amdgcn_readlane(kw.last, 31);
+  const int kt_begin = p.doc_off ? key_window(p.doc_off, p.n_docs, row0, S, p.causal).first / BK : 0;
+  const int kt_end = key_window(p.doc_off, p.n_docs, last_row, S, p.causal).last / BK + 1;
 
   floatx16 acc[NDB];
 #pragma unroll
@@ -142,15 +151,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdParams<T> p) {
     }
   };
 
-  load_tile(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
+  load_tile(kt_begin);
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     __syncthreads();
     store_tile();
     __syncthreads();
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kt + 1 < kt_end) load_tile(kt + 1);
 
     const int key0 = kt * BK;
-    const bool active = (wrow0 < S) && (!p.causal || key0 <= wrow0 + 31);
+    const bool active = (wrow0 < S) && key0 + BK - 1 >= w_first_min && key0 <= w_last_max;
     if (!active) continue;
 
     floatx16 s[2], dp[2];
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdParams<T> p) {
       }
     }
 
-    const bool need_mask = (p.causal && key0 + BK - 1 > wrow0) || (key0 + BK > S);
+    const bool need_mask = key0 < w_first_max || key0 + BK - 1 > w_last_min;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(BwdParams<T> p) {
         float pij = __builtin_amdgcn_exp2f(fmaf(s[b][j], p.scale_log2, -lse2));
         if (need_mask) {
           const int key = key0 + b * 32 + c_row(j, half);
-          if ((p.causal && key > my_row) || key >= S) pij = 0.f;
+          if (key < kw.first || key > kw.last) pij = 0.f;
         }
         s[b][j] = pij * (dp[b][j] + nD);  // dS^T
       }
@@ -297,9 +306,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdParams<T> p) {
     }
   }
 
-  const int n_qb = (S + BQ - 1) / BQ;
-  const int qb0 = p.causal ? key0 / BQ : 0;
-  const int steps_per_head = n_qb - qb0;
+  // Query rows that attend to this lane's key, [rw.first, rw.last]; both
+  // bounds grow with the key, so lanes 0 and 31 give the wave's extremes and
+  // the workgroup's first and last keys its row-block range [qb0, qb_top].
+  const int last_key = min(S, key0 + BKV) - 1;
+  DocSpan rw = row_window(p.doc_off, p.n_docs, min(my_key, S - 1), S, p.causal);
+  if (p.causal) rw.first = my_key;  // a key past the end has no rows
+  const int w_first_min = __builtin_amdgcn_readlane(rw.first, 0);
+  const int w_first_max = __builtin_amdgcn_readlane(rw.first, 31);
+  const int w_last_min = __builtin_amdgcn_readlane(rw.last, 0);
+  const int w_last_max = __builtin_amdgcn_readlane(rw.last, 31);
+  const int qb0 = row_window(p.doc_off, p.n_docs, key0, S, p.causal).first / BQ;
+  const int qb_top = row_window(p.doc_off, p.n_docs, last_key, S, p.causal).last / BQ;
+  const int steps_per_head = qb_top - qb0 + 1;
   const int n_steps = p.heads_per_kv * steps_per_head;
 
   uint4 qreg[VPT], oreg[VPT];
@@ -356,8 +375,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdParams<T> p) {
     if (step + 1 < n_steps) load_block(step + 1);
 
     const int r0 = qb * BQ;
-    const bool active = key_ok || (wkey0 < S);
-    if (!active || (p.causal && r0 + BQ - 1 < wkey0)) continue;
+    const bool active = (wkey0 < S) && r0 + BQ - 1 >= w_first_min && r0 <= w_last_max;
+    if (!active) continue;
 
     floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
@@ -368,7 +387,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdParams<T> p) {
       mma32(dp, oa, vf[ks]);
     }
 
-    const bool need_mask = (p.causal && r0 < wkey0 + 31) || (r0 + BQ > S);
+    const bool need_mask = r0 < w_first_max || r0 + BQ - 1 > w_last_min;
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg) {
       const floatx4 l4 = *reinterpret_cast<const floatx4*>(sL + jg * 8 + half * 4);
@@ -379,7 +398,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(BwdParams<T> p) {
         float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l4[e]));
         if (need_mask) {
           const int row = r0 + c_row(j, half);
-          if ((p.causal && my_key > row) || row >= S) pij = 0.f;
+          if (row < rw.first || row > rw.last) pij = 0.f;
         }
         s[j] = pij;                     // P
         dp[j] = pij * (dp[j] + d4[e]);  // dS

@@ -38,6 +38,8 @@ struct FwdParams {
   int heads_per_kv;  // chunk head hl reads pool kv head hl / heads_per_kv
   int n_qtiles;      // ceil(S / 128)
   int causal;
+  const int* doc_off;  // packed-document offsets o_0..o_n (device), or null
+  int n_docs;          // n
   float scale_log2;  // tau * log2(e)
 };
 
@@ -97,8 +99,17 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdParams<T> p) {
       qf[ks] = F{};
   }
 
+  // Keys this lane's row attends to, [kw.first, kw.last]; both bounds grow
+  // with the row, so lanes 0 and 31 give the wave's extremes and the
+  // workgroup's first and last rows its key-tile range.
   const int last_row = min(S, row0 + BQ) - 1;
-  const int n_kt = p.causal ? (last_row / BK + 1) : ((S + BK - 1) / BK);
+  const DocSpan kw = key_window(p.doc_off, p.n_docs, min(my_row, S - 1), S, p.causal);
+  const int w_first_min = __builtin_amdgcn_readlane(kw.first, 0);
+  const int w_first_max = __builtin_amdgcn_readlane(kw.first, 31);
+  const int w_last_min = __builtin_amdgcn_readlane(kw.last, 0);
+  const int w_last_max = __builtin_amdgcn_readlane(kw.last, 31);
+  const int kt_begin = p.doc_off ? key_window(p.doc_off, p.n_docs, row0, S, p.causal).first / BK : 0;
+  const int kt_end = key_window(p.doc_off, p.n_docs, last_row, S, p.causal).last / BK + 1;
 
   floatx16 o_acc[NDB];
 #pragma unroll
@@ -138,15 +149,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdParams<T> p) {
     }
   };
 
-  load_tile(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
+  load_tile(kt_begin);
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     __syncthreads();  // every wave is done with the previous tile
     store_tile();
     __syncthreads();
-    if (kt + 1 < n_kt) load_tile(kt + 1);  // in flight while this tile computes
+    if (kt + 1 < kt_end) load_tile(kt + 1);  // in flight while this tile computes
 
     const int key0 = kt * BK;
-    const bool active = (wrow0 < S) && (!p.causal || key0 <= wrow0 + 31);
+    const bool active = (wrow0 < S) && key0 + BK - 1 >= w_first_min && key0 <= w_last_max;
     if (!active) continue;
 
     // S^T = K Q^T: two 32-key blocks.
@@ -161,14 +172,14 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdParams<T> p) {
       }
     }
 
-    const bool need_mask = (p.causal && key0 + BK - 1 > wrow0) || (key0 + BK > S);
+    const bool need_mask = key0 < w_first_max || key0 + BK - 1 > w_last_min;
     if (need_mask) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = key0 + b * 32 + c_row(j, half);
-          if ((p.causal && key > my_row) || key >= S) s[b][j] = NEG_INF;
+          if (key < kw.first || key > kw.last) s[b][j] = NEG_INF;
         }
     }
 

@@ -91,4 +91,51 @@ __device__ __forceinline__ float wave_xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Packed documents (MaxText article on long-context training, the note that
+// several samples packed into one sequence need no padding): offsets
+// o_0 = 0 <= o_1 <= ... <= o_n = S in device memory; document m holds
+// positions o_m .. o_{m+1} - 1 and a position attends only within its own
+// document. doc_span(i) returns the first and last position of the document
+// holding position i (0 <= i < S) by binary search. It reads only o_0 .. o_n,
+// and its results are clamped to [0, i] and [i, S - 1], so offsets that break
+// the rules give wrong numbers but never an access outside the sequence.
+struct DocSpan {
+  int first, last;
+};
+__device__ __forceinline__ DocSpan doc_span(const int* __restrict__ off, int n, int i, int S) {
+  int lo = 0, hi = n;  // o_lo <= i < o_hi for well-formed offsets
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= i)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return {min(max(off[lo], 0), i), max(min(off[lo + 1] - 1, S - 1), i)};
+}
+
+// Keys that query row i attends to, [first, last]: up to the row itself when
+// causal, and inside the row's document when off is set.
+__device__ __forceinline__ DocSpan key_window(const int* __restrict__ off, int n, int i, int S, int causal) {
+  DocSpan w = {0, causal ? i : S - 1};
+  if (off) {
+    const DocSpan d = doc_span(off, n, i, S);
+    w.first = d.first;
+    if (!causal) w.last = d.last;
+  }
+  return w;
+}
+
+// Query rows that attend to key j, [first, last]: from the key itself when
+// causal, and inside the key's document when off is set.
+__device__ __forceinline__ DocSpan row_window(const int* __restrict__ off, int n, int j, int S, int causal) {
+  DocSpan w = {causal ? j : 0, S - 1};
+  if (off) {
+    const DocSpan d = doc_span(off, n, j, S);
+    if (!causal) w.first = d.first;
+    w.last = d.last;
+  }
+  return w;
+}
+
 }  // namespace upipe

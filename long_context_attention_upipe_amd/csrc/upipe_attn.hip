@@ -53,6 +53,8 @@ struct Problem {
   int heads_per_kv;  // q heads of one chunk that share a kv head = min(hc, G)
   int nkv;           // kv heads one chunk reads = max(1, hc / G)
   size_t es;         // element size
+  const int32_t* doc_off = nullptr;  // packed-document offsets (device), or null
+  int n_docs = 0;
 };
 
 int validate(int64_t S, int Hq, int Hkv, int d, int hc, int causal, int dtype, Problem* pr) {
@@ -272,6 +274,8 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     fp.heads_per_kv = pr.heads_per_kv;
     fp.n_qtiles = n_qtiles;
     fp.causal = pr.causal;
+    fp.doc_off = pr.doc_off;
+    fp.n_docs = pr.n_docs;
     fp.scale_log2 = scale * kLog2e;
     timed(K_FWD, st, [&] {
       if constexpr (std::is_same<T, bf16>::value)
@@ -353,6 +357,8 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     bp.n_qtiles = n_qtiles;
     bp.n_ktiles = n_ktiles;
     bp.causal = pr.causal;
+    bp.doc_off = pr.doc_off;
+    bp.n_docs = pr.n_docs;
     bp.acc_load = !c.first_for_kv;
     bp.finalize = c.last_for_kv;
     bp.scale = scale;
@@ -399,11 +405,27 @@ size_t upipe_attn_bwd_workspace_bytes(int64_t S, int Hq, int Hkv, int d, int hea
   return bwd_pool(pr).total;
 }
 
-int upipe_attn_fwd(const void* q, const void* k, const void* v, void* out, void* out_lo, float* lse, int64_t S,
-                   int Hq, int Hkv, int d, int head_chunk, int causal, int dtype, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Packed-document arguments: a device array of n_docs + 1 offsets, or none.
+int validate_docs(const int32_t* doc_offsets, int n_docs, Problem* pr) {
+  if (!doc_offsets) return fail(UPIPE_EINVAL, "doc_offsets is NULL");
+  if (n_docs < 1) return fail(UPIPE_EINVAL, "n_docs must be >= 1 (got %d)", n_docs);
+  if (reinterpret_cast<uintptr_t>(doc_offsets) % 4) return fail(UPIPE_EINVAL, "doc_offsets is not 4-byte aligned");
+  pr->doc_off = doc_offsets;
+  pr->n_docs = n_docs;
+  return UPIPE_OK;
+}
+
+int fwd_entry(const void* q, const void* k, const void* v, void* out, void* out_lo, float* lse, int64_t S, int Hq,
+              int Hkv, int d, int head_chunk, int causal, const int32_t* doc_offsets, int n_docs, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream) {
   Problem pr;
   if (int rc = validate(S, Hq, Hkv, d, head_chunk, causal, dtype, &pr)) return rc;
+  if (doc_offsets || n_docs)
+    if (int rc = validate_docs(doc_offsets, n_docs, &pr)) return rc;
   const void* ptrs[] = {q, k, v, out, lse, workspace};
   const char* names[] = {"q", "k", "v", "out", "lse", "workspace"};
   for (int i = 0; i < 6; ++i) {
@@ -427,12 +449,14 @@ int upipe_attn_fwd(const void* q, const void* k, const void* v, void* out, void*
   return run_fwd<float, 64>(pr, q, k, v, out, out_lo, lse, ws, st);
 }
 
-int upipe_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* out_lo,
-                   const void* dout, const float* lse, void* dq, void* dk, void* dv, int64_t S, int Hq, int Hkv,
-                   int d, int head_chunk, int causal, int dtype, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+int bwd_entry(const void* q, const void* k, const void* v, const void* out, const void* out_lo, const void* dout,
+              const float* lse, void* dq, void* dk, void* dv, int64_t S, int Hq, int Hkv, int d, int head_chunk,
+              int causal, const int32_t* doc_offsets, int n_docs, int dtype, void* workspace,
+              size_t workspace_bytes, void* stream) {
   Problem pr;
   if (int rc = validate(S, Hq, Hkv, d, head_chunk, causal, dtype, &pr)) return rc;
+  if (doc_offsets || n_docs)
+    if (int rc = validate_docs(doc_offsets, n_docs, &pr)) return rc;
   const void* ptrs[] = {q, k, v, out, dout, lse, dq, dk, dv, workspace};
   const char* names[] = {"q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "workspace"};
   for (int i = 0; i < 10; ++i) {
@@ -454,6 +478,42 @@ int upipe_attn_bwd(const void* q, const void* k, const void* v, const void* out,
   }
   if (d == 128) return run_bwd<float, 128>(pr, q, k, v, out, out_lo, dout, lse, dq, dk, dv, ws, st);
   return run_bwd<float, 64>(pr, q, k, v, out, out_lo, dout, lse, dq, dk, dv, ws, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int upipe_attn_fwd(const void* q, const void* k, const void* v, void* out, void* out_lo, float* lse, int64_t S,
+                   int Hq, int Hkv, int d, int head_chunk, int causal, int dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return fwd_entry(q, k, v, out, out_lo, lse, S, Hq, Hkv, d, head_chunk, causal, nullptr, 0, dtype, workspace,
+                   workspace_bytes, stream);
+}
+
+int upipe_attn_fwd_docs(const void* q, const void* k, const void* v, void* out, void* out_lo, float* lse,
+                        int64_t S, int Hq, int Hkv, int d, int head_chunk, int causal, const int32_t* doc_offsets,
+                        int n_docs, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!doc_offsets && !n_docs) return fail(UPIPE_EINVAL, "doc_offsets is NULL");
+  return fwd_entry(q, k, v, out, out_lo, lse, S, Hq, Hkv, d, head_chunk, causal, doc_offsets, n_docs, dtype,
+                   workspace, workspace_bytes, stream);
+}
+
+int upipe_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* out_lo,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv, int64_t S, int Hq, int Hkv,
+                   int d, int head_chunk, int causal, int dtype, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return bwd_entry(q, k, v, out, out_lo, dout, lse, dq, dk, dv, S, Hq, Hkv, d, head_chunk, causal, nullptr, 0,
+                   dtype, workspace, workspace_bytes, stream);
+}
+
+int upipe_attn_bwd_docs(const void* q, const void* k, const void* v, const void* out, const void* out_lo,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int64_t S, int Hq,
+                        int Hkv, int d, int head_chunk, int causal, const int32_t* doc_offsets, int n_docs,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!doc_offsets && !n_docs) return fail(UPIPE_EINVAL, "doc_offsets is NULL");
+  return bwd_entry(q, k, v, out, out_lo, dout, lse, dq, dk, dv, S, Hq, Hkv, d, head_chunk, causal, doc_offsets,
+                   n_docs, dtype, workspace, workspace_bytes, stream);
 }
 
 int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks, int32_t* q_head0, int32_t* kv_head0,

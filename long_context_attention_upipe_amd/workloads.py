@@ -11,6 +11,12 @@ sequence lengths the talk reaches (3M tokens with the technique stack, 5M
 with UPipe) ["Road to 5 Million Tokens" talk summary, Summary and Chapters;
 MaxText long-context article, strategy table: one kv head per chip at most].
 The head dim (128) is not fixed by the pages; 128 is the Llama-3 value.
+
+Packed documents (MaxText long-context article: several samples packed into
+one long sequence) come as offsets 0 = o_0 <= ... <= o_n = S. The pages give
+no length distribution; the workloads here draw document lengths
+log-uniformly between a minimum and a maximum (every scale equally likely),
+seeded, and cut the last document at S.
 """
 
 from __future__ import annotations
@@ -36,6 +42,7 @@ class Workload:
     dout_scaled: bool  # dO ~ N(0,1)/sqrt(S) instead of N(0,1)
     seed: int
     causal: bool = True
+    doc_lengths: tuple = ()  # (min, max) of log-uniform document lengths; () = one sequence
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -48,6 +55,8 @@ WORKLOADS = {
     "llama8b_share_s1m": Workload("llama8b_share_s1m", 1048576, 4, 1, 128, "bf16", (1, 2, 4), True, 3000),
     "llama8b_share_s3m": Workload("llama8b_share_s3m", 3145728, 4, 1, 128, "bf16", (1, 2, 4), True, 4000),
     "share32b_s5m": Workload("share32b_s5m", 5242880, 8, 1, 128, "bf16", (1, 2, 4, 8), True, 5000),
+    "llama8b_share_s1m_docs": Workload("llama8b_share_s1m_docs", 1048576, 4, 1, 128, "bf16", (1, 2, 4), True, 6000,
+                                       doc_lengths=(1024, 262144)),
 }
 
 
@@ -55,6 +64,38 @@ def custom(S, Hq, Hkv, d, dtype="bf16", seed=7, dout_scaled=False, causal=True, 
     """A workload of arbitrary shape (used by parity tests at small sizes)."""
     return Workload(name or f"S{S}_Hq{Hq}_Hkv{Hkv}_d{d}_{dtype}", S, Hq, Hkv, d, dtype,
                     (1,), dout_scaled, seed, causal)
+
+
+def loguniform_doc_offsets(S: int, min_len: int, max_len: int, seed: int) -> np.ndarray:
+    """Offsets (int32, 0 .. S) of documents whose lengths are drawn seeded and
+    log-uniformly in [min_len, max_len]; the last document is cut at S."""
+    rng = np.random.default_rng(seed)
+    offs = [0]
+    while offs[-1] < S:
+        n = int(round(math.exp(rng.uniform(math.log(min_len), math.log(max_len)))))
+        offs.append(min(S, offs[-1] + max(1, n)))
+    return np.asarray(offs, dtype=np.int32)
+
+
+def doc_offsets(w: Workload):
+    """The workload's document offsets (int32 numpy), or None for one sequence."""
+    if not w.doc_lengths:
+        return None
+    return loguniform_doc_offsets(w.S, w.doc_lengths[0], w.doc_lengths[1], w.seed + 9)
+
+
+def doc_boundary_rows(offsets, n_docs: int, seed: int) -> np.ndarray:
+    """Seeded sample of positions at document edges: the first two and last
+    two positions of up to ``n_docs`` documents."""
+    rng = np.random.default_rng(seed)
+    offs = np.asarray(offsets, dtype=np.int64)
+    nonempty = [m for m in range(len(offs) - 1) if offs[m + 1] > offs[m]]
+    pick = rng.choice(nonempty, size=min(n_docs, len(nonempty)), replace=False)
+    rows = set()
+    for m in pick:
+        a, b = int(offs[m]), int(offs[m + 1])
+        rows.update(r for r in (a, a + 1, b - 2, b - 1) if a <= r < b)
+    return np.array(sorted(rows), dtype=np.int64)
 
 
 def _normal(shape, seed, device, dtype, slab_dim=None):

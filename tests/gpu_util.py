@@ -18,16 +18,19 @@ def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run(q, k, v, do, head_chunk, causal=True, ws=None):
-    """Forward then backward on the current device; returns device tensors."""
+def run(q, k, v, do, head_chunk, causal=True, ws=None, doc_offsets=None):
+    """Forward then backward on the current device; returns device tensors.
+    ``doc_offsets`` (int32 device tensor) selects the packed-document calls."""
     S, Hq, d = q.shape
     Hkv = k.shape[1]
     if ws is None:
         ws = up.workspace(S, Hq, Hkv, d, head_chunk, q.dtype, q.device, "both")
-    out, lse, out_lo = up.attention_forward(q, k, v, head_chunk=head_chunk, causal=causal, ws=ws)
+    out, lse, out_lo = up.attention_forward(q, k, v, head_chunk=head_chunk, causal=causal, ws=ws,
+                                            doc_offsets=doc_offsets)
     res = {"out": out, "lse": lse}
     if do is not None:
-        dq, dk, dv = up.attention_backward(q, k, v, out, do, lse, out_lo, head_chunk=head_chunk, causal=causal, ws=ws)
+        dq, dk, dv = up.attention_backward(q, k, v, out, do, lse, out_lo, head_chunk=head_chunk, causal=causal, ws=ws,
+                                           doc_offsets=doc_offsets)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return res

@@ -168,3 +168,58 @@ def test_binding_rejects_mismatched_shapes(name, bad):
     with pytest.raises(L.UpipeError, match=f"{name} has shape"):
         L._require_shapes(q, named)
     L._require_shapes(q, [(n, torch.empty(exp), exp) for n, _, exp in named])
+
+
+def _fwd_docs(offsets=FAKE, n_docs=3, **kw):
+    a = dict(S=256, Hq=4, Hkv=1, d=128, hc=1, causal=1, dtype=0, ws_bytes=1 << 40)
+    a.update(kw)
+    return L.lib().upipe_attn_fwd_docs(FAKE, FAKE, FAKE, FAKE, None, FAKE, a["S"], a["Hq"], a["Hkv"], a["d"], a["hc"],
+                                       a["causal"], offsets, n_docs, a["dtype"], FAKE, a["ws_bytes"], None)
+
+
+def _bwd_docs(offsets=FAKE, n_docs=3, **kw):
+    a = dict(S=256, Hq=4, Hkv=1, d=128, hc=1, causal=1, dtype=0, ws_bytes=1 << 40)
+    a.update(kw)
+    return L.lib().upipe_attn_bwd_docs(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, a["S"], a["Hq"],
+                                       a["Hkv"], a["d"], a["hc"], a["causal"], offsets, n_docs, a["dtype"], FAKE,
+                                       a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("call", [_fwd_docs, _bwd_docs], ids=["fwd", "bwd"])
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(offsets=None), -1, "doc_offsets is NULL"),
+    (dict(offsets=None, n_docs=0), -1, "doc_offsets is NULL"),
+    (dict(n_docs=0), -1, "n_docs must be >= 1"),
+    (dict(n_docs=-2), -1, "n_docs must be >= 1"),
+    (dict(offsets=ctypes.c_void_p(0x10002)), -1, "not 4-byte aligned"),
+    (dict(hc=3), -1, "must divide Hq"),
+    (dict(ws_bytes=16), -3, "workspace too small"),
+])
+def test_document_entry_points_reject_bad_arguments(call, kw, status, msg):
+    assert call(**kw) == status
+    assert msg in L.upipe_last_error()
+
+
+@pytest.mark.parametrize("offsets,msg", [
+    ([0, 10, 64], None),
+    ([0, 0, 64, 64], None),
+    ([0, 64], None),
+    ([1, 10, 64], "rise"),
+    ([0, 10, 63], "rise"),
+    ([0, 30, 20, 64], "rise"),
+    ([64], "at least two"),
+])
+def test_binding_checks_document_offsets(offsets, msg):
+    """The library reads the offsets on the device only, so the binding checks
+    their values (here on CPU tensors; the same code runs on device tensors)."""
+    import torch
+
+    q = torch.empty(64, 4, 32)
+    t = torch.tensor(offsets, dtype=torch.int32)
+    if msg is None:
+        assert L._require_docs(q, t) == len(offsets) - 1
+    else:
+        with pytest.raises(L.UpipeError, match=msg):
+            L._require_docs(q, t)
+    with pytest.raises(L.UpipeError, match="int32"):
+        L._require_docs(q, t.long())
