@@ -5,9 +5,12 @@
 //  * K/V (forward, dQ) and Q/dO (dK/dV) tiles go global -> LDS directly, into
 //    double-buffered XOR-swizzled row-major tiles (lds_tiles.hpp): one barrier
 //    per tile, no staging registers;
-//  * operands that contract over a tile's rows (V^T in P V, K^T in dS K,
-//    dO^T in dV, Q^T in dK) are read transposed from the same row-major tile
-//    with ds_read_b64_tr_b16 instead of keeping a second, transposed copy;
+//  * operands that contract over a tile's rows (K^T in dS K, dO^T in dV, Q^T
+//    in dK) are read transposed from the same row-major tile with
+//    ds_read_b64_tr_b16 instead of keeping a second, transposed copy; the
+//    forward, whose only use of V is V^T, gets V transposed in the pool
+//    instead, so all of its reads are ds_read_b128 (twice the bytes per LDS
+//    instruction of the transposed read);
 //  * register budgets fit two waves per SIMD, so one wave's softmax VALU
 //    work overlaps the other wave's MFMAs.
 #pragma once
@@ -24,6 +27,10 @@ namespace upipe {
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p) {
   constexpr int BQ = 128, BK = 64, NKS = D / 16, NDB = D / 32;
+  // K tiles [BK keys][D]; V tiles transposed, [D][BK positions] (pack_vt_kernel
+  // blocks, one contiguous block per tile), so both operands are read as
+  // 16-byte row fragments. Both layouts
+  // are conflict-free for row reads (kSwzAll).
   __shared__ __attribute__((aligned(1024))) bf16 sK[2][BK * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV[2][BK * D];
 
@@ -39,7 +46,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
   const size_t head_elems = (size_t)S * D;
   const bf16* __restrict__ Q = p.q + (size_t)hl * head_elems;
   const bf16* __restrict__ K = p.k + (size_t)kvl * head_elems;
-  const bf16* __restrict__ V = p.v + (size_t)kvl * head_elems;
+  const bf16* __restrict__ VT = p.v + (size_t)kvl * D * p.Sp;
 
   const int row0 = qt * BQ;
   const int wrow0 = row0 + wave * 32;
@@ -57,8 +64,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
   const int kt_begin = p.doc_off ? key_window(p.doc_off, p.n_docs, row0, S, p.causal).first / BK : 0;
   const int kt_end = key_window(p.doc_off, p.n_docs, last_row, S, p.causal).last / BK + 1;
 
-  tile_load_async<D, BK, 4>(sK[kt_begin & 1], K, kt_begin * BK, S, wave, lane);
-  tile_load_async<D, BK, 4>(sV[kt_begin & 1], V, kt_begin * BK, S, wave, lane);
+  tile_load_async<D, BK, 4, kSwzAll>(sK[kt_begin & 1], K, kt_begin * BK, S, wave, lane);
+  tile_load_rows_async<BK, D, 4, kSwzAll>(sV[kt_begin & 1], VT + (size_t)kt_begin * BK * D, BK, wave, lane);
 
   bf16x8 qf[NKS];
 #pragma unroll
@@ -77,8 +84,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < kt_end) {
-      tile_load_async<D, BK, 4>(sK[cur ^ 1], K, (kt + 1) * BK, S, wave, lane);
-      tile_load_async<D, BK, 4>(sV[cur ^ 1], V, (kt + 1) * BK, S, wave, lane);
+      tile_load_async<D, BK, 4, kSwzAll>(sK[cur ^ 1], K, (kt + 1) * BK, S, wave, lane);
+      tile_load_rows_async<BK, D, 4, kSwzAll>(sV[cur ^ 1], VT + (size_t)(kt + 1) * BK * D, BK, wave, lane);
     }
     const int key0 = kt * BK;
     const bool active = (wrow0 < S) && key0 + BK - 1 >= w_first_min && key0 <= w_last_max;
@@ -88,7 +95,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
       for (int b = 0; b < 2; ++b) {
         s[b] = floatx16{};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) mma32(s[b], tile_row_frag<D>(sK[cur], b * 32 + col, 2 * ks + half), qf[ks]);
+        for (int ks = 0; ks < NKS; ++ks)
+          mma32(s[b], tile_row_frag<D, kSwzAll>(sK[cur], b * 32 + col, 2 * ks + half), qf[ks]);
       }
       const bool need_mask = key0 < w_first_max || key0 + BK - 1 > w_last_min;
       if (need_mask) {
@@ -135,8 +143,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
           for (int e = 0; e < 8; ++e) pv[e] = s[b][st * 8 + e];
           const bf16x8 pf = to_frag(pv, bf16());
 #pragma unroll
+          // V^T row db*32+col, positions 32b + 16st + 8half .. +7: the keys
+          // 32b + 16st + c_row(e, half), e = 0..7, in the order of pf
           for (int db = 0; db < NDB; ++db)
-            mma32(o_acc[db], tile_tr_frag<D>(sV[cur], b * 32 + st * 16, db * 32, lane), pf);
+            mma32(o_acc[db], tile_row_frag<BK, kSwzAll>(sV[cur], db * 32 + col, 4 * b + 2 * st + half), pf);
         }
     }
     wait_vm();

@@ -28,7 +28,8 @@ template <typename T>
 struct FwdParams {
   const T* q;        // pool: chunk q rows, [hc][S][D]
   const T* k;        // pool: chunk kv heads, [nkv][S][D]
-  const T* v;        // pool: [nkv][S][D]
+  const T* v;        // pool: fp32 [nkv][S][D]; bf16 transposed, [nkv][Sp/64][D][64] (pack_vt_kernel)
+  int Sp;            // bf16: S rounded up to 64
   T* o;              // pool: chunk output rows, [hc][S][D]
   T* o_lo;           // caller out_lo at the chunk's first head (row stride H*D), or null
   int H;             // caller heads per row (out_lo row stride in heads)

@@ -44,6 +44,42 @@ __global__ __launch_bounds__(256) void unpack_heads_kernel(const uint4* __restri
   }
 }
 
+// Transposed pack of bf16 V heads for the forward kernel, whose only use of V
+// is as the operand of O^T += V^T P^T, contracting over keys. Keys go in
+// blocks of 64; block b of head hl is a contiguous [D][64] matrix
+//   dst[hl][b][c][p] = src[64b + j(p)][h0 + hl][c],  p < 64,
+// with j(p) = (p & ~15) | perm16(p & 15): inside each group of 16 keys the
+// positions follow the key order of a P fragment taken from score registers,
+// so the 8 keys one lane contributes to an MFMA step sit in 16 consecutive
+// bytes of a row. Keys >= S hold 0 (the last block is padded). Blocks are
+// contiguous so that a key tile is one 16 KiB (d = 128) run of memory, not D
+// rows a whole sequence apart. One workgroup moves one block through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void pack_vt_kernel(const bf16* __restrict__ src, bf16* __restrict__ dst, int S,
+                                                     int Sp, int H, int h0) {
+  constexpr int VPR = D / 8;  // 16-byte vectors per key row
+  __shared__ __attribute__((aligned(16))) bf16 t[64][D + 8];
+  const int kb = blockIdx.x, hl = blockIdx.y, tid = threadIdx.x;
+  for (int i = tid; i < 64 * VPR; i += 256) {
+    const int r = i / VPR, v = i % VPR;
+    const int key = kb * 64 + r;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (key < S) x = *reinterpret_cast<const uint4*>(src + ((size_t)key * H + h0 + hl) * D + v * 8);
+    *reinterpret_cast<uint4*>(&t[r][v * 8]) = x;
+  }
+  __syncthreads();
+  for (int i = tid; i < D * 8; i += 256) {
+    const int c = i / 8, pv = i % 8;
+    bf16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pos = pv * 8 + e;
+      y[e] = t[(pos & ~15) | perm16(pos & 15)][c];
+    }
+    *reinterpret_cast<bf16x8*>(dst + (size_t)hl * D * Sp + ((size_t)kb * D + c) * 64 + pv * 8) = y;
+  }
+}
+
 // One group of D/EPV lanes per (row, head): reads a 16-byte slice of out and
 // dout each, writes the dout slice into the pool, reduces the dot product.
 template <typename T, int D>

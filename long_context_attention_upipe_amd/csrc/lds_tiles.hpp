@@ -107,6 +107,28 @@ __device__ __forceinline__ void tile_load_async(bf16* tile, const bf16* g, int g
   }
 }
 
+// Issue the copy of a ROWS x W block of a row-major bf16 matrix with row
+// stride ld elements, starting at g, into `tile` (same LDS layout as
+// tile_load_async with D = W). Every element must lie inside the matrix: the
+// caller pads. Asynchronous, completed like tile_load_async.
+template <int W, int ROWS, int NWAVES, int M = kSwzTr>
+__device__ __forceinline__ void tile_load_rows_async(bf16* tile, const bf16* g, size_t ld, int wave, int lane) {
+  constexpr int CPR = W / 8;
+  constexpr int SLOTS = ROWS * CPR;
+  constexpr int INSTR = SLOTS / 64;
+  static_assert(SLOTS % 64 == 0, "tile must be a whole number of 1 KiB wave copies");
+  static_assert(INSTR % NWAVES == 0, "wave copies must split evenly");
+#pragma unroll
+  for (int k = 0; k < INSTR / NWAVES; ++k) {
+    const int i = k * NWAVES + wave;
+    const int slot = i * 64 + lane;
+    const int r = slot / CPR, pos = slot % CPR;
+    const int c = pos ^ swz<W, M>(r);
+    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)r * ld + c * 8), (lds_void*)(tile + i * 512), 16, 0,
+                                     0);
+  }
+}
+
 // Wait for this wave's outstanding global loads (including LDS copies).
 __device__ __forceinline__ void wait_vm() {
   // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima (no wait)

@@ -116,6 +116,13 @@ std::vector<Chunk> plan(const Problem& pr) {
 struct FwdPool {
   size_t q, o, k, v, total;
 };
+// The forward's V: bf16 heads are stored transposed in blocks of 64 keys,
+// [Sp/64][D][64] with Sp = S rounded up to 64 (pack_vt_kernel); fp32 heads as
+// [S][D].
+int64_t vt_len(const Problem& pr) { return (pr.S + 63) / 64 * 64; }
+size_t vt_bytes(const Problem& pr) {
+  return pr.dtype == UPIPE_BF16 ? (size_t)vt_len(pr) * pr.d * pr.es : (size_t)pr.S * pr.d * pr.es;
+}
 FwdPool fwd_pool(const Problem& pr) {
   const size_t U = (size_t)pr.S * pr.d * pr.es;  // one head, whole sequence
   FwdPool p;
@@ -123,7 +130,7 @@ FwdPool fwd_pool(const Problem& pr) {
   p.q = off; off += align_up(pr.hc * U);
   p.o = off; off += align_up(pr.hc * U);
   p.k = off; off += align_up(pr.nkv * U);
-  p.v = off; off += align_up(pr.nkv * U);
+  p.v = off; off += align_up(pr.nkv * vt_bytes(pr));
   p.total = off;
   return p;
 }
@@ -252,8 +259,12 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
                            pr.Hkv, c.kv_head0, c.n_kv, vpr);
       });
       timed(K_PACK, st, [&] {
-        hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)v, (uint4*)Vc, S,
-                           pr.Hkv, c.kv_head0, c.n_kv, vpr);
+        if constexpr (std::is_same<T, bf16>::value)
+          hipLaunchKernelGGL((pack_vt_kernel<D>), dim3((unsigned)(vt_len(pr) / 64), c.n_kv), dim3(256), 0, st,
+                             (const bf16*)v, (bf16*)Vc, S, (int)vt_len(pr), pr.Hkv, c.kv_head0);
+        else
+          hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)v, (uint4*)Vc,
+                             S, pr.Hkv, c.kv_head0, c.n_kv, vpr);
       });
     }
     const size_t nq = (size_t)S * pr.hc * vpr;
@@ -262,6 +273,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
                          pr.Hq, c.q_head0, pr.hc, vpr);
     });
     FwdParams<T> fp;
+    fp.Sp = (int)vt_len(pr);
     fp.q = Qc;
     fp.k = Kc;
     fp.v = Vc;

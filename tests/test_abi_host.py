@@ -66,10 +66,12 @@ def test_pool_grows_strictly_with_head_chunk(S, Hq, Hkv, d, hcs, dtype):
     assert all(a < b for a, b in zip(bwd, bwd[1:])), bwd
     es = 2 if dtype == 0 else 4
     U = S * d * es
-    # the forward pool holds the chunk's q and out rows and its kv heads
+    # the forward pool holds the chunk's q and out rows and its kv heads; bf16 v
+    # heads are stored transposed with rows padded to a multiple of 64 positions
+    Uv = ((S + 63) // 64 * 64 if dtype == 0 else S) * d * es
     for hc, n in zip(hcs, fwd):
         nkv = max(1, hc // (Hq // Hkv))
-        assert 2 * hc * U + 2 * nkv * U <= n < 2 * hc * U + 2 * nkv * U + 4096
+        assert 2 * hc * U + nkv * (U + Uv) <= n < 2 * hc * U + nkv * (U + Uv) + 4096
 
 
 def test_pool_at_5m_tokens_matches_plan():
