@@ -72,7 +72,9 @@ typedef enum {
 /*
  * Bytes of the fixed buffer pool that upipe_attn_fwd needs (the buffers that
  * every head chunk reuses: the chunk's q and out rows, head-major, and its
- * kv head(s)). Returns 0 and sets upipe_last_error() on invalid arguments.
+ * kv head(s); for bf16 the v head is held transposed in blocks of 64 keys,
+ * padded to a multiple of 64 positions). Returns 0 and sets
+ * upipe_last_error() on invalid arguments.
  */
 size_t upipe_attn_fwd_workspace_bytes(int64_t S, int Hq, int Hkv, int d,
                                       int head_chunk, int dtype);
