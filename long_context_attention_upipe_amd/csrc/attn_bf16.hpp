@@ -241,46 +241,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
     }
     const int key0 = kt * BK;
     const bool active = (wrow0 < S) && key0 + BK - 1 >= w_first_min && key0 <= w_last_max;
-    const bool need_mask = key0 < w_first_max || key0 + BK - 1 > w_last_min;
-    if (active && !need_mask) {
-      // Unmasked tile, software-pipelined over its two 32-key blocks: both
-      // blocks' score and dP MFMAs are issued first, so block 0's softmax
-      // runs while block 1's MFMAs execute, and block 1's softmax while block
-      // 0's dQ MFMAs do. Every accumulator sees its MFMAs in the same order as
-      // in the block-by-block loop below.
-      floatx16 s0 = floatx16{}, s1 = floatx16{}, dp0, dp1;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        dp0[j] = nD;
-        dp1[j] = nD;
-      }
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        mma32(s0, tile_row_frag<D>(sK[cur], col, 2 * ks + half), qf[ks]);
-        mma32(dp0, tile_row_frag<D>(sV[cur], col, 2 * ks + half), df[ks]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        mma32(s1, tile_row_frag<D>(sK[cur], 32 + col, 2 * ks + half), qf[ks]);
-        mma32(dp1, tile_row_frag<D>(sV[cur], 32 + col, 2 * ks + half), df[ks]);
-      }
-      auto ds_and_dq = [&](floatx16& sb, const floatx16& dpb, int b) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sb[j] = __builtin_amdgcn_exp2f(fmaf(sb[j], p.scale_log2, -l2)) * dpb[j];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          floatx8 d8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) d8[e] = sb[st * 8 + e];
-          const bf16x8 dsf = to_frag(d8, bf16());
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            mma32(acc[db], tile_tr_frag<D>(sK[cur], b * 32 + st * 16, db * 32, lane), dsf);
-        }
-      };
-      ds_and_dq(s0, dp0, 0);
-      ds_and_dq(s1, dp1, 1);
-    } else if (active) {
+    if (active) {
+      const bool need_mask = key0 < w_first_max || key0 + BK - 1 > w_last_min;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         // dP starts from this lane's row -D, so the MFMAs yield dP - D
