@@ -28,15 +28,15 @@ from oracle.attention import backward_cols_dkdv, backward_rows_dq, forward_rows
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def _run_chunks(w, q, k, v, do, head_chunks):
+def _run_chunks(w, q, k, v, do, head_chunks, causal=True):
     results = {}
     for hc in head_chunks:
-        print(f"   {w.name}: head_chunk={hc}", flush=True)
+        print(f"   {w.name}: head_chunk={hc} causal={causal}", flush=True)
         ws = up.workspace(w.S, w.Hq, w.Hkv, w.d, hc, q.dtype, q.device, "both")
         up.upipe_profile_reset()
         up.upipe_profile_enable(True)
-        out, lse, out_lo = up.attention_forward(q, k, v, head_chunk=hc, causal=True, ws=ws)
-        dq, dk, dv = up.attention_backward(q, k, v, out, do, lse, out_lo, head_chunk=hc, causal=True, ws=ws)
+        out, lse, out_lo = up.attention_forward(q, k, v, head_chunk=hc, causal=causal, ws=ws)
+        dq, dk, dv = up.attention_backward(q, k, v, out, do, lse, out_lo, head_chunk=hc, causal=causal, ws=ws)
         up.wait_reporting(f"head_chunk={hc}", q.device, prefix="  ")
         up.upipe_profile_enable(False)
         up.upipe_profile_reset()
@@ -109,6 +109,46 @@ def test_llama8b_share_128k_sampled_4096_rows():
 def test_llama8b_share_1m_sampled_4096_rows():
     w = WORKLOADS["llama8b_share_s1m"]
     _check(w, w.head_chunks, 4096, 128, 512)
+
+
+def test_llama8b_share_128k_non_causal_sampled_rows():
+    """Non-causal attention (every row sees all S keys) at 131,072 tokens: O,
+    LSE and dQ at 2048 sampled rows, exact in O(S*d) each; bit-identity across
+    head_chunk; the column sums sum_j dK_j = 0 and sum_j dV_j = sum of dO over
+    the group, which hold without a mask too. Sampled dK/dV keys are not
+    checked here: without the causal mask every row contributes to every key,
+    so exact values need every row's LSE and D, O(S^2 d)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w = WORKLOADS["llama8b_share_s128k"]
+    print(f"\n  case {w.name} non-causal S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d}", flush=True)
+    dev = torch.device("cuda:0")
+    q, k, v, do = make_inputs(w, device=dev)
+    r = _run_chunks(w, q, k, v, do, w.head_chunks, causal=False)
+    rows = sample_rows(w.S, 2048, seed=w.seed + 17)
+    rows_t = torch.from_numpy(rows).to(dev)
+    kc, vc = f64(k), f64(v)
+    qr, dor = f64(q[rows_t]), f64(do[rows_t])
+    parts = interleaved_parts(len(rows), 64)
+    fwd = oracle_parallel(lambda p: forward_rows(qr[p], kc, vc, rows[p], causal=False), parts, "forward rows")
+    o_ref, l_ref = np.empty_like(qr), np.empty((w.Hq, len(rows)))
+    for p, (o, lse) in zip(parts, fwd):
+        o_ref[p], l_ref[:, p] = o, lse
+    assert_close("out", f64(r["out"][rows_t]), o_ref, w.dtype)
+    assert_close("lse", f64(r["lse"][:, rows_t]), l_ref, w.dtype)
+    dqs = oracle_parallel(lambda p: backward_rows_dq(qr[p], kc, vc, dor[p], rows[p], causal=False), parts,
+                          "dq rows")
+    dq_ref = np.empty_like(qr)
+    for p, dq in zip(parts, dqs):
+        dq_ref[p] = dq
+    assert_close("dq", f64(r["dq"][rows_t]), dq_ref, w.dtype)
+    G = w.Hq // w.Hkv
+    dk_sum, dk_abs = sum64(r["dk"], (0,)), sum64(r["dk"].abs(), (0,))
+    dv_sum = sum64(r["dv"], (0,))
+    for g in range(w.Hkv):
+        assert np.all(np.abs(dk_sum[g]) <= 1e-2 * dk_abs[g] + 1e-4)
+        ref = sum64(do[:, g * G:(g + 1) * G, :], (0, 1))
+        assert_close("dvsum", dv_sum[g], ref, w.dtype)
 
 
 @pytest.mark.skipif(os.environ.get("UPIPE_TEST_5M") != "1",
