@@ -185,3 +185,60 @@ def test_llama8b_share_1m_docs_sampled():
         keys_t = torch.from_numpy(keys).to(dev)
         assert_close("dk", f64(r["dk"][keys_t]), dk_ref, w.dtype)
         assert_close("dv", f64(r["dv"][keys_t]), dv_ref, w.dtype)
+
+
+@pytest.mark.slow
+def test_llama8b_share_1m_docs_non_causal_sampled():
+    """1,048,576 tokens in 16 documents, non-causal (a position sees its whole
+    document): O, LSE and dQ at 1024 sampled rows plus the edges of every
+    document (each non-causal row costs its whole document in the oracle);
+    dK and dV at 64 keys in each of the two shortest documents (without the
+    causal mask a key's gradient takes every row of its document, so exact
+    values stay cheap only in short ones); outputs bit-identical across
+    head_chunk 1, 2, 4."""
+    dev = _dev()
+    w = WORKLOADS["llama8b_share_s1m_docs"]
+    offsets = doc_offsets(w)
+    print(f"\n  case {w.name} non-causal S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} docs={len(offsets) - 1}", flush=True)
+    q, k, v, do = make_inputs(w, device=dev)
+    offs_t = torch.from_numpy(offsets).to(dev)
+    r = None
+    for hc in w.head_chunks:
+        print(f"   head_chunk={hc}", flush=True)
+        cur = run(q, k, v, do, hc, causal=False, doc_offsets=offs_t)
+        if r is None:
+            r = cur
+        else:
+            for name in cur:
+                assert bit_equal(cur[name], r[name]), f"{name}: head_chunk {hc} differs"
+            del cur
+
+    rows = np.union1d(sample_rows(w.S, 1024, seed=w.seed + 17), doc_boundary_rows(offsets, len(offsets), w.seed + 18))
+    rows_t = torch.from_numpy(rows).to(dev)
+    kc, vc = f64(k), f64(v)
+    qr, dor = f64(q[rows_t]), f64(do[rows_t])
+    parts = interleaved_parts(len(rows), 64)
+    fwd = oracle_parallel(lambda p: forward_rows(qr[p], kc, vc, rows[p], causal=False, doc_offsets=offsets), parts,
+                          "forward rows")
+    o_ref, l_ref = np.empty_like(qr), np.empty((w.Hq, len(rows)))
+    for p, (o, lse) in zip(parts, fwd):
+        o_ref[p], l_ref[:, p] = o, lse
+    assert_close("out", f64(r["out"][rows_t]), o_ref, w.dtype)
+    assert_close("lse", f64(r["lse"][:, rows_t]), l_ref, w.dtype)
+    dqs = oracle_parallel(lambda p: backward_rows_dq(qr[p], kc, vc, dor[p], rows[p], causal=False,
+                                                     doc_offsets=offsets), parts, "dq rows")
+    dq_ref = np.empty_like(qr)
+    for p, dq in zip(parts, dqs):
+        dq_ref[p] = dq
+    assert_close("dq", f64(r["dq"][rows_t]), dq_ref, w.dtype)
+
+    print("   oracle: keys in the shortest documents", flush=True)
+    lengths = np.diff(offsets)
+    q32, do32 = q.float().cpu().numpy(), do.float().cpu().numpy()
+    for m in np.argsort(lengths, kind="stable")[:2]:
+        start = int(offsets[m])
+        keys = np.arange(start, start + min(64, int(lengths[m])), dtype=np.int64)
+        dk_ref, dv_ref = backward_cols_dkdv(q32, kc, vc, do32, keys, causal=False, doc_offsets=offsets)
+        keys_t = torch.from_numpy(keys).to(dev)
+        assert_close("dk", f64(r["dk"][keys_t]), dk_ref, w.dtype)
+        assert_close("dv", f64(r["dv"][keys_t]), dv_ref, w.dtype)
