@@ -22,7 +22,7 @@ import torch
 
 import long_context_attention_upipe_amd as up
 from gpu_util import assert_close, bit_equal, f64, interleaved_parts, oracle_parallel, sum64
-from long_context_attention_upipe_amd.workloads import WORKLOADS, make_inputs, sample_rows, tail_keys
+from long_context_attention_upipe_amd.workloads import WORKLOADS, Workload, make_inputs, sample_rows, tail_keys
 from oracle.attention import backward_cols_dkdv, backward_rows_dq, forward_rows
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -109,6 +109,17 @@ def test_llama8b_share_128k_sampled_4096_rows():
 def test_llama8b_share_1m_sampled_4096_rows():
     w = WORKLOADS["llama8b_share_s1m"]
     _check(w, w.head_chunks, 4096, 128, 512)
+
+
+def test_head_dim_64_two_kv_heads_ragged_131k_sampled_rows():
+    """Head dim 64 (its own kernel instantiations and LDS layouts), two kv
+    heads (Hq = 8, Hkv = 2) and a length that is no multiple of any tile
+    (131,109 = 2^17 + 37), at head_chunk 1, 2, 4 (chunks inside one kv group)
+    and 8 (both groups in one chunk): the same sampled-row, tail-key and
+    column-sum checks as the workloads above, and bit-identity across
+    head_chunk."""
+    w = Workload("d64_gqa2_s131109", 131109, 8, 2, 64, "bf16", (1, 2, 4, 8), True, 7000)
+    _check(w, w.head_chunks, 2048, 128, 1024)
 
 
 def test_llama8b_share_128k_non_causal_sampled_rows():
