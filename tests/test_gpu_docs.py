@@ -192,10 +192,12 @@ def test_llama8b_share_1m_docs_non_causal_sampled():
     """1,048,576 tokens in 16 documents, non-causal (a position sees its whole
     document): O, LSE and dQ at 1024 sampled rows plus the edges of every
     document (each non-causal row costs its whole document in the oracle);
-    dK and dV at 64 keys in each of the two shortest documents (without the
+    dK and dV at 64 keys in each of the four shortest documents (without the
     causal mask a key's gradient takes every row of its document, so exact
-    values stay cheap only in short ones); outputs bit-identical across
-    head_chunk 1, 2, 4."""
+    values stay cheap only in short ones). A document's results are those of
+    the document run alone (pinned in the oracle's tests), so the keys' oracle
+    runs on each document's slice. Outputs bit-identical across head_chunk 1,
+    2, 4."""
     dev = _dev()
     w = WORKLOADS["llama8b_share_s1m_docs"]
     offsets = doc_offsets(w)
@@ -234,11 +236,11 @@ def test_llama8b_share_1m_docs_non_causal_sampled():
 
     print("   oracle: keys in the shortest documents", flush=True)
     lengths = np.diff(offsets)
-    q32, do32 = q.float().cpu().numpy(), do.float().cpu().numpy()
-    for m in np.argsort(lengths, kind="stable")[:2]:
-        start = int(offsets[m])
-        keys = np.arange(start, start + min(64, int(lengths[m])), dtype=np.int64)
-        dk_ref, dv_ref = backward_cols_dkdv(q32, kc, vc, do32, keys, causal=False, doc_offsets=offsets)
-        keys_t = torch.from_numpy(keys).to(dev)
+    for m in np.argsort(lengths, kind="stable")[:4]:
+        start, end = int(offsets[m]), int(offsets[m + 1])
+        keys = np.arange(min(64, end - start), dtype=np.int64)
+        dk_ref, dv_ref = backward_cols_dkdv(f64(q[start:end]), kc[start:end], vc[start:end], f64(do[start:end]), keys,
+                                            causal=False)
+        keys_t = torch.from_numpy(keys + start).to(dev)
         assert_close("dk", f64(r["dk"][keys_t]), dk_ref, w.dtype)
         assert_close("dv", f64(r["dv"][keys_t]), dv_ref, w.dtype)
