@@ -39,7 +39,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
   const int col = lane & 31, half = lane >> 5;
   const int S = p.S;
 
-  const int t = blockIdx.x;
+  // Workgroups go to the 8 XCDs round-robin (index mod 8). Inside each
+  // full block of 64 indices, XCD x takes the 8 consecutive tiles 8x .. 8x+7
+  // of the block, so the workgroups that share one L2 stream the same K/V
+  // tiles; the order across blocks stays heaviest first.
+  const int t0 = blockIdx.x;
+  const int t = (t0 / 64 + 1) * 64 <= (int)gridDim.x ? (t0 & ~63) | ((t0 & 7) << 3) | ((t0 >> 3) & 7) : t0;
   const int qt = p.causal ? (p.n_qtiles - 1 - t / p.hc) : (t / p.hc);
   const int hl = t % p.hc;
   const int kvl = hl / p.heads_per_kv;
@@ -190,7 +195,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
   const int col = lane & 31, half = lane >> 5;
   const int S = p.S;
 
-  const int t = blockIdx.x;
+  // XCD-aware order, as in the forward.
+  const int t0 = blockIdx.x;
+  const int t = (t0 / 64 + 1) * 64 <= (int)gridDim.x ? (t0 & ~63) | ((t0 & 7) << 3) | ((t0 >> 3) & 7) : t0;
   const int qt = p.causal ? (p.n_qtiles - 1 - t / p.hc) : (t / p.hc);
   const int hl = t % p.hc;
   const int kvl = hl / p.heads_per_kv;
@@ -328,7 +335,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
   const int col = lane & 31, half = lane >> 5;
   const int S = p.S;
 
-  const int t = blockIdx.x;
+  // XCD-aware order, as in the forward: each XCD takes runs of 8 consecutive
+  // key tiles, which walk the same query blocks.
+  const int t0 = blockIdx.x;
+  const int t = (t0 / 64 + 1) * 64 <= (int)gridDim.x ? (t0 & ~63) | ((t0 & 7) << 3) | ((t0 >> 3) & 7) : t0;
   const int kt = t / p.nkv;
   const int g = t % p.nkv;
   const size_t head_elems = (size_t)S * D;
