@@ -13,7 +13,13 @@ Q K^T and P V; bwd 10*d: the Q K^T recompute, dP, dV, dK and dQ). Masked
 pairs, softmax work and any extra recompute are not counted.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--head-chunk HC] [--sweep] [--no-cpu-baseline]
+                    [--head-chunk HC] [--no-sweep] [--no-residual-run] [--no-cpu-baseline]
+
+After the timed headline run, every other head_chunk of the workload runs
+(1 warmup + 2 steps each by default) so the line carries the chunk-size
+trade-off: TFLOP/s and peak HBM per head_chunk (`head_chunk_sweep`). One more
+step at the headline head_chunk runs without out_lo (the forward's stored
+rounding residual of out) to report peak HBM when D comes from out alone.
 """
 
 from __future__ import annotations
@@ -42,17 +48,41 @@ ALGO_FLOPS_PER_PAIR_D = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 2}
 EXEC_FLOPS_PER_PAIR_D = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 6}
 
 
+# The device code of the three attention kernels is defined by these headers
+# alone (tiles, grid mapping, arithmetic); HBM counters taken on other sources
+# do not describe them.
+ATTN_KERNEL_SOURCES = ("attn_bf16.hpp", "attn_fwd.hpp", "attn_bwd.hpp", "common.hpp", "lds_tiles.hpp")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources the library is built from."""
+    """sha256 over the HIP headers that define the attention kernels."""
     import hashlib
 
     d = os.path.join(ROOT, "long_context_attention_upipe_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hpp", ".hip")):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(ATTN_KERNEL_SOURCES):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
+
+
+def algo_bytes(kernel: str, w, head_chunk: int) -> int:
+    """Algorithmic HBM bytes of one launch: every input read once, every output
+    written once, for the head_chunk query heads of a chunk and their kv heads.
+    forward: Q, K, V in, O, LSE out; dK/dV and dQ: Q, dO, K, V, LSE, D in and
+    their own outputs out."""
+    es = 2 if w.dtype == "bf16" else 4
+    G = w.Hq // w.Hkv
+    nkv = max(1, head_chunk // G)
+    U = w.S * w.d * es
+    rows = head_chunk * w.S * 4  # one fp32 per (row, head)
+    if kernel == "attn_fwd":
+        return 2 * head_chunk * U + 2 * nkv * U + rows
+    if kernel == "attn_bwd_dkdv":
+        return 2 * head_chunk * U + 2 * nkv * U + 2 * rows + 2 * nkv * U
+    if kernel == "attn_bwd_dq":
+        return 2 * head_chunk * U + 2 * nkv * U + 2 * rows + head_chunk * U
+    raise KeyError(kernel)
 
 
 def measured_traffic(kernel: str, workload: str, head_chunk: int):
@@ -129,7 +159,7 @@ def cpu_baseline(w, q, k, v, do, s_prefix: int):
     }
 
 
-def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
+def run_one(w, head_chunk: int, steps: int, warmup: int, dev, residual: bool = True):
     import torch
 
     import long_context_attention_upipe_amd as up
@@ -141,7 +171,8 @@ def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
     base = torch.cuda.memory_allocated(dev)
     q, k, v, do = make_inputs(w, device=dev)
     out = torch.empty_like(q)
-    out_lo = torch.empty_like(q) if q.dtype == torch.bfloat16 else None  # out's rounding residual, for D
+    # out's rounding residual, for D (residual=False: D from out alone)
+    out_lo = torch.empty_like(q) if (residual and q.dtype == torch.bfloat16) else None
     lse = torch.empty((w.Hq, w.S), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     code = up.dtype_code(q.dtype)
@@ -226,6 +257,7 @@ def run_one(w, head_chunk: int, steps: int, warmup: int, dev):
         "fwd_tflops": f_fwd / (fwd_ms / 1e3) / 1e12,
         "bwd_tflops": f_bwd / (bwd_ms / 1e3) / 1e12,
         "peak_hbm_gib": peak_alloc / GIB,
+        "out_lo_gib": (out_lo.numel() * out_lo.element_size() / GIB) if out_lo is not None else 0.0,
         "workspace_gib": ws_bytes / GIB,
         "kernels": kernels,
     }
@@ -240,6 +272,8 @@ def roofline(w, res, head_chunk):
     name = max(attn, key=lambda n: attn[n]["total_ms_per_step"])
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
     achieved = attn[name]["algo_tflops"]
+    traffic = measured_traffic(name, w.name, head_chunk)
+    ab = algo_bytes(name, w, head_chunk)
     return {
         "kernel": name,
         "bound": "mfma",
@@ -247,7 +281,9 @@ def roofline(w, res, head_chunk):
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": measured_traffic(name, w.name, head_chunk),
+        "traffic": traffic,
+        "algo_bytes": ab,
+        "traffic_over_algo_bytes": round(traffic / ab, 1) if traffic else None,
         "per_unit": f"{ALGO_FLOPS_PER_PAIR_D[name]}*d FLOP per unmasked (row, key) pair and head; "
                     f"{head_chunk} heads x "
                     + ("S(S+1)/2" if not w.doc_lengths else "the sum over documents of L(L+1)/2")
@@ -262,8 +298,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="llama8b_share_s1m")
     ap.add_argument("--head-chunk", type=int, default=None, help="default: the workload's smallest")
-    ap.add_argument("--sweep", action="store_true", help="also run every head_chunk of the workload")
-    ap.add_argument("--sweep-chunks", default=None, help="comma-separated head_chunk values for --sweep")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the head_chunk sweep (by default every other head_chunk of the workload runs after "
+                         "the headline, --sweep-warmup/--sweep-steps each, for the peak-HBM curve)")
+    ap.add_argument("--sweep-chunks", default=None, help="comma-separated head_chunk values for the sweep")
+    ap.add_argument("--sweep-steps", type=int, default=2)
+    ap.add_argument("--sweep-warmup", type=int, default=1)
+    ap.add_argument("--no-residual-run", action="store_true",
+                    help="skip the one-step run without out_lo (peak HBM when D comes from out alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prefix", type=int, default=32768, help="positions in the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -301,20 +343,32 @@ def main():
     res, tensors = run_one(w, hc, args.steps, args.warmup, dev)
     print(f"[bench] timed: {res['ms_per_step']:.1f} ms/step, {res['tflops']:.1f} TFLOP/s", file=sys.stderr,
           flush=True)
+    del tensors  # every run draws its own inputs (same seeds): keep one set resident at a time
     sweep = []
-    if args.sweep:
+    if not args.no_sweep:
         chunks = [int(x) for x in args.sweep_chunks.split(",")] if args.sweep_chunks else list(w.head_chunks)
         for h in chunks:
-            r = res if h == hc else run_one(w, h, args.steps, args.warmup, dev)[0]
-            sweep.append({k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items()
-                          if k_ != "kernels"})
+            r = res if h == hc else run_one(w, h, args.sweep_steps, args.sweep_warmup, dev)[0]
+            entry = {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in r.items() if k_ != "kernels"}
+            entry["steps"] = args.steps if h == hc else args.sweep_steps
+            sweep.append(entry)
             print(f"[bench] sweep head_chunk={h}: {r['tflops']:.1f} TFLOP/s peak {r['peak_hbm_gib']:.2f} GiB",
                   file=sys.stderr, flush=True)
+    no_res = None
+    if not args.no_residual_run and w.dtype == "bf16":
+        r = run_one(w, hc, 1, 0, dev, residual=False)[0]
+        no_res = {"head_chunk": hc, "peak_hbm_gib": round(r["peak_hbm_gib"], 4), "tflops": round(r["tflops"], 2),
+                  "steps": 1, "warmup": 0}
+        print(f"[bench] without out_lo: peak {r['peak_hbm_gib']:.2f} GiB", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
-        q, k, v, do = tensors
+        from long_context_attention_upipe_amd.workloads import make_inputs
+
+        # the same seeded inputs, drawn again on the device and cut to the prefix
+        q, k, v, do = (t[:min(args.cpu_prefix, w.S)] for t in make_inputs(w, device=dev))
         cpu = cpu_baseline(w, q, k, v, do, min(args.cpu_prefix, w.S))
+        del q, k, v, do
         print(f"[bench] cpu oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads", file=sys.stderr,
               flush=True)
 
@@ -345,6 +399,8 @@ def main():
         "fwd_tflops": round(res["fwd_tflops"], 2),
         "bwd_tflops": round(res["bwd_tflops"], 2),
         "peak_hbm_gib": round(res["peak_hbm_gib"], 3),
+        "out_lo_gib": round(res["out_lo_gib"], 3),
+        "peak_hbm_without_out_lo": no_res,
         "workspace_gib": round(res["workspace_gib"], 3),
         "roofline": roofline(w, res, hc),
         "cpu_baseline": cpu,

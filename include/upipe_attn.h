@@ -36,7 +36,7 @@
  *     UPIPE_FP32 (all fp32). lse is always fp32.
  *   - Supported: d in {64, 128}; Hq % Hkv == 0; head_chunk divides Hq and
  *     either divides G = Hq/Hkv or is a multiple of it; causal in {0, 1};
- *     1 <= S and S*d < 2^31.
+ *     1 <= S, S*d < 2^31 and every tensor below 2^48 bytes.
  *   - stream: a hipStream_t (NULL = the null stream). All work is enqueued on
  *     it and the call returns without synchronising.
  *   - Errors: every argument is validated on the host before anything is
@@ -91,12 +91,35 @@ size_t upipe_attn_bwd_workspace_bytes(int64_t S, int Hq, int Hkv, int d,
                                       int head_chunk, int dtype);
 
 /*
+ * Bytes of one workspace that serves both upipe_attn_fwd and upipe_attn_bwd
+ * (called one after the other, as in training): the larger of the two values
+ * above. This is the size of the fixed buffer pool of the chunked method
+ * (talk summary, Chapters: heads processed in batches reuse one buffer); it
+ * rises strictly with head_chunk and does not depend on Hq beyond that.
+ * Returns 0 and sets upipe_last_error() on invalid arguments.
+ */
+size_t upipe_attn_workspace_bytes(int64_t S, int Hq, int Hkv, int d,
+                                  int head_chunk, int dtype);
+
+/*
+ * The chunk-size trade-off (talk summary, Chapters: the chunk-size chapter;
+ * talk digest, Plan: pick the chunk from the memory left): returns the
+ * largest valid head_chunk whose workspace (upipe_attn_workspace_bytes) fits
+ * in budget_bytes -- larger chunks take fewer, wider launches and more
+ * memory. Host only. Returns UPIPE_EWORKSPACE if even head_chunk 1 does not
+ * fit, or another negative status for invalid arguments.
+ */
+int upipe_attn_pick_head_chunk(int64_t S, int Hq, int Hkv, int d, int dtype,
+                               size_t budget_bytes);
+
+/*
  * Forward. Reads q, k, v; writes out and lse (every element). Runs the head
  * chunks in ascending head order on `stream`, each through the same workspace.
  *
  * out_lo (bf16 only; may be NULL): receives, element by element, the bf16
  * rounding residual of out, bf16(o - out) where o is the fp32 result, same
- * layout as out. Handing it to upipe_attn_bwd lets the backward form
+ * layout as out (so it costs one more [S, Hq, d] bf16 tensor of caller
+ * memory, e.g. 10 GiB at S = 5,242,880, Hq = 8, d = 128). Handing it to upipe_attn_bwd lets the backward form
  * D = <dout, o> from o to about 16 significant bits instead of 8. That
  * matters for rows whose softmax is peaked (every causal row near the start
  * of the sequence): there dP_ij - D_i cancels and a D taken from the rounded
@@ -166,6 +189,60 @@ int upipe_attn_bwd_docs(const void* q, const void* k, const void* v,
                         int causal, const int32_t* doc_offsets, int n_docs,
                         int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bf16 GEMM with fp32 accumulation on the MFMA units (the projections around
+ * the chunked attention use it; exported so it can be checked on its own):
+ *   C[M, N] = A[M, K] B[K, N]   (accumulate != 0, fp32 C only: C += A B)
+ * Each operand is described by its contiguous index -- K if *_kmajor != 0
+ * (A stored [M][K], B stored [N][K] as a torch Linear weight), else M or N
+ * (A stored [K][M], B stored [K][N]) -- and
+ *   element (c, o) at ptr + (c / blk) * blk_stride + o * ld + (c % blk),
+ * c the contiguous index, o the other one; blk <= 0 means one block (a plain
+ * row-major matrix), blk > 0 lets the contiguous index run in blocks (a
+ * head-major [heads][S][d] buffer read as one [S][heads * d] matrix). C is
+ *   C[m, n] at c + (n / c_blk) * c_blk_stride + m * ldc + (n % c_blk),
+ * bf16 (c_dtype = UPIPE_BF16, rounded to nearest even) or fp32.
+ * Requirements: K a multiple of 64; N a multiple of 8; an M- (N-)contiguous
+ * operand needs M (N) a multiple of 8; every ld, block length and block
+ * stride a multiple of 8 elements; pointers 16-byte aligned; M, N >= 1.
+ * Device pointers, owned by the caller; the extents the layouts reach must lie
+ * inside the caller's buffers (not checkable here: plain pointers). Errors as
+ * for the attention calls; the work is enqueued on `stream`.
+ */
+int upipe_gemm_bf16(const void* a, int64_t lda, int64_t a_blk, int64_t a_blk_stride, int a_kmajor,
+                    const void* b, int64_t ldb, int64_t b_blk, int64_t b_blk_stride, int b_kmajor,
+                    void* c, int64_t ldc, int64_t c_blk, int64_t c_blk_stride, int c_dtype,
+                    int accumulate, int M, int N, int K, void* stream);
+
+/*
+ * Attention block, forward, chunked around the heads (talk summary,
+ * Chapters: in the Q&A the head batching is said to target the layer's Q, K
+ * and V, full-sequence tensors; the chapter on processing heads in batches).
+ * Per head chunk, in ascending head order, through one fixed pool:
+ *   q_h = x Wq_h^T, k_g = x Wk_g^T, v_g = x Wv_g^T    (rounded to bf16)
+ *   o_h = causal GQA attention of the chunk's heads   (as upipe_attn_fwd)
+ *   y  += o_h Wo_h^T, one head at a time, in fp32
+ * so no q, k, v or o of all heads over the whole sequence is ever formed.
+ *   x   [S, Dm] bf16, the layer input (token-major)
+ *   wq  [Hq*d, Dm], wk, wv [Hkv*d, Dm], wo [Dm, Hq*d] bf16, torch Linear
+ *       layout [out_features, in_features], no bias; head h owns rows
+ *       h*d .. h*d+d-1 of wq and columns h*d .. of wo, kv head g rows g*d ..
+ *       of wk and wv (GQA: q head h reads kv head h / (Hq/Hkv))
+ *   y   [S, Dm] fp32, written (not accumulated into)
+ *   out [S, Hq, d] bf16 or NULL: the attention output, kept only if given
+ *   lse [Hq, S] fp32, natural log, as upipe_attn_fwd
+ * Dm a multiple of 64; d in {64, 128}; head_chunk as for upipe_attn_fwd. y,
+ * out and lse are bit-identical across head_chunk. Workspace:
+ * upipe_attn_block_fwd_workspace_bytes (the chunk's q and o rows, its kv
+ * heads' k, v and transposed v rows); it rises with head_chunk only.
+ */
+size_t upipe_attn_block_fwd_workspace_bytes(int64_t S, int Dm, int Hq, int Hkv, int d,
+                                            int head_chunk);
+int upipe_attn_block_fwd(const void* x, const void* wq, const void* wk, const void* wv,
+                         const void* wo, float* y, void* out, float* lse,
+                         int64_t S, int Dm, int Hq, int Hkv, int d, int head_chunk,
+                         int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The head-chunk plan, for inspection (host only, no device work). Fills up to

@@ -10,13 +10,18 @@ from ._lib import (  # noqa: F401
     UPIPE_FP32,
     UpipeError,
     dtype_code,
+    upipe_attn_block_fwd,
+    upipe_attn_block_fwd_workspace_bytes,
     upipe_attn_bwd,
     upipe_attn_bwd_docs,
     upipe_attn_bwd_workspace_bytes,
     upipe_attn_fwd,
     upipe_attn_fwd_docs,
     upipe_attn_fwd_workspace_bytes,
+    upipe_attn_pick_head_chunk,
     upipe_attn_plan,
+    upipe_attn_workspace_bytes,
+    upipe_gemm_bf16,
     upipe_last_error,
     upipe_profile_completed,
     upipe_profile_enable,

@@ -46,11 +46,22 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_fwd_workspace_bytes.restype = sz
     L.upipe_attn_bwd_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
     L.upipe_attn_bwd_workspace_bytes.restype = sz
+    L.upipe_attn_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.upipe_attn_workspace_bytes.restype = sz
+    L.upipe_attn_pick_head_chunk.argtypes = [i64, i32, i32, i32, i32, sz]
+    L.upipe_attn_pick_head_chunk.restype = i32
     L.upipe_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     L.upipe_attn_fwd.restype = i32
     L.upipe_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz,
                                  vp]
     L.upipe_attn_bwd.restype = i32
+    L.upipe_gemm_bf16.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, i32, i32, i32,
+                                  i32, i32, vp]
+    L.upipe_gemm_bf16.restype = i32
+    L.upipe_attn_block_fwd_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.upipe_attn_block_fwd_workspace_bytes.restype = sz
+    L.upipe_attn_block_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.upipe_attn_block_fwd.restype = i32
     # The packed-document entry points are bound when the loaded build has
     # them (UPIPE_ATTN_LIBRARY may name an older build); calling them on a
     # build without them raises AttributeError.
@@ -108,6 +119,22 @@ def upipe_attn_bwd_workspace_bytes(S, Hq, Hkv, d, head_chunk, dtype) -> int:
     if n == 0:
         raise UpipeError(-1, upipe_last_error())
     return n
+
+
+def upipe_attn_workspace_bytes(S, Hq, Hkv, d, head_chunk, dtype) -> int:
+    """Bytes of one workspace serving both the forward and the backward."""
+    n = lib().upipe_attn_workspace_bytes(S, Hq, Hkv, d, head_chunk, dtype)
+    if n == 0:
+        raise UpipeError(-1, upipe_last_error())
+    return n
+
+
+def upipe_attn_pick_head_chunk(S, Hq, Hkv, d, dtype, budget_bytes) -> int:
+    """Largest valid head_chunk whose workspace fits in ``budget_bytes``."""
+    rc = lib().upipe_attn_pick_head_chunk(S, Hq, Hkv, d, dtype, int(budget_bytes))
+    if rc < 0:
+        raise UpipeError(rc, upipe_last_error())
+    return rc
 
 
 def upipe_attn_plan(Hq, Hkv, head_chunk):
@@ -280,3 +307,74 @@ def upipe_profile_completed():
     total = ctypes.c_int(0)
     done = lib().upipe_profile_completed(ctypes.byref(total))
     return int(done), int(total.value)
+
+
+def upipe_gemm_bf16(a, a_layout, b, b_layout, c, c_layout, M, N, K, accumulate=False, stream=None) -> None:
+    """C[M, N] (+)= A[M, K] B[K, N] on the library's bf16 MFMA GEMM.
+
+    Each layout is a dict: ``ld`` (stride of the non-contiguous index),
+    ``kmajor`` (operands: K is the contiguous index), and optionally ``blk`` /
+    ``blk_stride`` (the contiguous index runs in blocks). The caller states
+    the layout; the library sees plain pointers, so the extent each layout
+    reaches is checked here against the tensor's storage."""
+    for name, t, lay, outer, dt in (("a", a, a_layout, M, torch.bfloat16), ("b", b, b_layout, N, torch.bfloat16),
+                                    ("c", c, c_layout, M, c.dtype)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != dt:
+            raise UpipeError(-1, f"{name}: a contiguous {dt} device tensor is required")
+        # (contiguous index extent, other index extent)
+        if name == "c":
+            contig, other = N, M
+        elif lay["kmajor"]:
+            contig, other = K, outer
+        else:
+            contig, other = outer, K
+        blk = lay.get("blk", 0) or contig
+        last = ((contig - 1) // blk) * lay.get("blk_stride", 0) + (other - 1) * lay["ld"] + ((contig - 1) % blk)
+        if last >= t.numel():
+            raise UpipeError(-1, f"{name}: the layout reaches element {last}, beyond the tensor's {t.numel()}")
+    code = UPIPE_FP32 if c.dtype == torch.float32 else UPIPE_BF16
+    with torch.cuda.device(a.device):
+        _check(lib().upipe_gemm_bf16(_ptr(a), a_layout["ld"], a_layout.get("blk", 0), a_layout.get("blk_stride", 0),
+                                     int(a_layout["kmajor"]), _ptr(b), b_layout["ld"], b_layout.get("blk", 0),
+                                     b_layout.get("blk_stride", 0), int(b_layout["kmajor"]), _ptr(c),
+                                     c_layout["ld"], c_layout.get("blk", 0), c_layout.get("blk_stride", 0), code,
+                                     int(bool(accumulate)), M, N, K, _stream_handle(stream)))
+
+
+def upipe_attn_block_fwd_workspace_bytes(S, Dm, Hq, Hkv, d, head_chunk) -> int:
+    n = lib().upipe_attn_block_fwd_workspace_bytes(S, Dm, Hq, Hkv, d, head_chunk)
+    if n == 0:
+        raise UpipeError(-1, upipe_last_error())
+    return n
+
+
+def upipe_attn_block_fwd(x, wq, wk, wv, wo, y, out, lse, n_q_heads, n_kv_heads, head_chunk, causal, workspace,
+                         stream=None) -> None:
+    """Attention block forward, chunk by chunk: q, k, v of the chunk's heads
+    from x, causal GQA attention, and the chunk's share of y = o Wo^T.
+    x [S, Dm] bf16; wq [Hq*d, Dm], wk, wv [Hkv*d, Dm], wo [Dm, Hq*d] bf16
+    (torch Linear layout); y [S, Dm] fp32; out [S, Hq, d] bf16 or None;
+    lse [Hq, S] fp32."""
+    if x.dim() != 2 or wq.dim() != 2:
+        raise UpipeError(-1, "x and the weights must be 2-D")
+    S, Dm = x.shape
+    Hq, Hkv = int(n_q_heads), int(n_kv_heads)
+    if wq.shape[0] % Hq:
+        raise UpipeError(-1, "wq's rows must be Hq * d")
+    d = wq.shape[0] // Hq
+    _require((x, wq, wk, wv, wo) + ((out,) if out is not None else ()), torch.bfloat16)
+    _require((y, lse), torch.float32)
+    _require((workspace,), torch.uint8)
+    for name, t, shape in (("wq", wq, (Hq * d, Dm)), ("wk", wk, (Hkv * d, Dm)), ("wv", wv, (Hkv * d, Dm)),
+                           ("wo", wo, (Dm, Hq * d)), ("y", y, (S, Dm)), ("out", out, (S, Hq, d)),
+                           ("lse", lse, (Hq, S)), ("workspace", workspace, (workspace.numel(),))):
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(shape):
+            raise UpipeError(-1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.device != x.device:
+            raise UpipeError(-1, f"{name} is on {t.device}, x on {x.device}")
+    with torch.cuda.device(x.device):
+        _check(lib().upipe_attn_block_fwd(_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(y), _ptr(out),
+                                          _ptr(lse), S, Dm, Hq, Hkv, d, int(head_chunk), int(causal),
+                                          _ptr(workspace), workspace.numel(), _stream_handle(stream)))

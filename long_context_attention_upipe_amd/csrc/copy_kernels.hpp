@@ -18,29 +18,41 @@
 
 namespace upipe {
 
+// Grid-stride loops of the copy kernels run over tokens with a 64-bit index
+// (S * nh * vpr can exceed 2^32 at multi-million-token lengths, where a 32-bit
+// grid-stride index would wrap and never end); each block iteration covers
+// max(1, 256 / per) whole tokens of per = nh * vpr vectors, so the divisions
+// inside a token stay 32-bit and small.
+
 // dst[hl][i][:] = src[i][h0 + hl][:]  (vpr = 16-byte vectors per row).
 __global__ __launch_bounds__(256) void pack_heads_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                         int S, int H, int h0, int nh, int vpr) {
-  const uint32_t total = (uint32_t)S * (uint32_t)nh * (uint32_t)vpr;
-  for (uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
-    const uint32_t v = idx % vpr;
-    const uint32_t r = idx / vpr;
-    const uint32_t hl = r % nh;
-    const uint32_t i = r / nh;
-    dst[((size_t)hl * S + i) * vpr + v] = src[((size_t)i * H + h0 + hl) * vpr + v];
+  const int per = nh * vpr;
+  const int tpi = max(1, 256 / per);  // tokens per block iteration
+  for (int64_t t0 = (int64_t)blockIdx.x * tpi; t0 < S; t0 += (int64_t)gridDim.x * tpi) {
+    for (int e = threadIdx.x; e < tpi * per; e += 256) {
+      const int64_t i = t0 + e / per;
+      if (i >= S) break;
+      const int rem = e % per;
+      const int hl = rem / vpr, v = rem % vpr;
+      dst[((size_t)hl * S + i) * vpr + v] = src[((size_t)i * H + h0 + hl) * vpr + v];
+    }
   }
 }
 
 // dst[i][h0 + hl][:] = src[hl][i][:]
 __global__ __launch_bounds__(256) void unpack_heads_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                           int S, int H, int h0, int nh, int vpr) {
-  const uint32_t total = (uint32_t)S * (uint32_t)nh * (uint32_t)vpr;
-  for (uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
-    const uint32_t v = idx % vpr;
-    const uint32_t r = idx / vpr;
-    const uint32_t hl = r % nh;
-    const uint32_t i = r / nh;
-    dst[((size_t)i * H + h0 + hl) * vpr + v] = src[((size_t)hl * S + i) * vpr + v];
+  const int per = nh * vpr;
+  const int tpi = max(1, 256 / per);
+  for (int64_t t0 = (int64_t)blockIdx.x * tpi; t0 < S; t0 += (int64_t)gridDim.x * tpi) {
+    for (int e = threadIdx.x; e < tpi * per; e += 256) {
+      const int64_t i = t0 + e / per;
+      if (i >= S) break;
+      const int rem = e % per;
+      const int hl = rem / vpr, v = rem % vpr;
+      dst[((size_t)i * H + h0 + hl) * vpr + v] = src[((size_t)hl * S + i) * vpr + v];
+    }
   }
 }
 
@@ -92,10 +104,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
   constexpr int TPR = D / EPV;  // lanes per row: 16 (bf16, d=128), 8, 16 or 32
   constexpr int RPB = 256 / TPR;
   const int sub = threadIdx.x % TPR;
-  const uint32_t total = (uint32_t)S * (uint32_t)nh;
-  for (uint32_t r = blockIdx.x * RPB + threadIdx.x / TPR; r < total; r += gridDim.x * RPB) {
-    const uint32_t hl = r % nh;
-    const uint32_t i = r / nh;
+  // Row slots of one block iteration: whole tokens, max(1, RPB / nh) of them,
+  // with a 64-bit token index (see the copy kernels above).
+  const int tpi = max(1, RPB / nh);
+  for (int64_t t0 = (int64_t)blockIdx.x * tpi; t0 < S; t0 += (int64_t)gridDim.x * tpi)
+  for (int slot = threadIdx.x / TPR; slot < tpi * nh; slot += RPB) {
+    const int64_t i = t0 + slot / nh;
+    if (i >= S) break;
+    const int hl = slot % nh;
     const size_t src = ((size_t)i * H + h0 + hl) * D + sub * EPV;
     const uint4 ov = *reinterpret_cast<const uint4*>(out + src);
     const uint4 dv = *reinterpret_cast<const uint4*>(dout + src);

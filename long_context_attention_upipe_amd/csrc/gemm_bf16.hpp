@@ -1,0 +1,183 @@
+// bf16 GEMM with fp32 accumulation on gfx950 MFMA, for the projections that
+// the chunked attention block runs around each head chunk (q, k, v of the
+// chunk's heads from the layer input, and the chunk's share of the output
+// projection), so that no tensor of every head over the whole sequence is
+// formed ("Road to 5 Million Tokens" talk summary, Chapters: the Q&A on which
+// tensors the head batching targets, the layer's Q, K and V).
+//
+//   C[M, N] = A[M, K] B[K, N]      (or C += ..., fp32 C only)
+//
+// Operands are addressed through a layout descriptor: each one is stored
+// with either its K index contiguous ("k-major", e.g. a token-major
+// activation [M][K] or a torch Linear weight [N][K]) or its M / N index
+// contiguous ("mn-major", [K][M] or [K][N]). The contiguous index may run in
+// blocks (a head-major [heads][S][d] buffer read as one [S][heads*d] matrix).
+// Tiles go global -> LDS directly (global_load_lds), double-buffered. Both
+// operand kinds are read in one k order: a P-fragment order in which the 8
+// values a lane supplies for a 16-deep MFMA step are k = 4h..4h+3 and
+// 8+4h..8+4h+3 (h = lane half); mn-major tiles give that order with the
+// transposed LDS read, k-major tiles with two 8-byte reads. So any pair of
+// layouts feeds v_mfma_f32_32x32x16_bf16 without a transposing copy.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "lds_tiles.hpp"
+
+namespace upipe {
+
+// Element (c, o) of an operand, c its contiguous index (K for k-major, M or N
+// for mn-major) and o the other one, lives at
+//   p + (c / blk) * blk_stride + o * ld + (c % blk).
+struct GemmOperand {
+  const bf16* p;
+  int64_t ld;          // stride of the other index, elements
+  int64_t blk;         // block length of the contiguous index (a multiple of 8)
+  int64_t blk_stride;  // distance between blocks, elements
+  int kmajor;          // 1: K contiguous; 0: M (or N) contiguous
+};
+
+// C[m, n] at p + (n / blk) * blk_stride + m * ldc + (n % blk).
+template <typename CT>
+struct GemmOut {
+  CT* p;
+  int64_t ldc;
+  int64_t blk;  // a multiple of 8
+  int64_t blk_stride;
+};
+
+template <typename CT>
+struct GemmParams {
+  GemmOperand a, b;
+  GemmOut<CT> c;
+  int M, N, K;     // K a multiple of 64; M, N, block lengths multiples of 8
+  int accumulate;  // fp32 C only: C += A B (else C = A B)
+};
+
+__device__ __forceinline__ const bf16* gemm_elem(const GemmOperand& op, int64_t c, int64_t o) {
+  return op.p + (c / op.blk) * op.blk_stride + o * op.ld + (c % op.blk);
+}
+
+// Copy one operand's slice of a K tile into LDS. k-major: [128 mn][64 k]
+// tile (row = mn); mn-major: [64 k][128 mn] tile (row = k). Indices past the
+// matrix (ragged M or N) are clamped to its last row or chunk: those lanes'
+// results are never stored.
+template <int MODE>
+__device__ __forceinline__ void gemm_load_tile(bf16* tile, const GemmOperand& op, int mn0, int MN, int k0, int wave,
+                                               int lane) {
+  if (op.kmajor) {
+    constexpr int D = 64, CPR = D / 8, INSTR = 128 * CPR / 64;
+#pragma unroll
+    for (int i0 = 0; i0 < INSTR / 4; ++i0) {
+      const int i = i0 * 4 + wave, slot = i * 64 + lane;
+      const int r = slot / CPR, pos = slot % CPR, c = pos ^ swz<D, MODE>(r);
+      const int mn = min(mn0 + r, MN - 1);
+      __builtin_amdgcn_global_load_lds((const void*)gemm_elem(op, (int64_t)k0 + c * 8, mn), (lds_void*)(tile + i * 512),
+                                       16, 0, 0);
+    }
+  } else {
+    constexpr int D = 128, CPR = D / 8, INSTR = 64 * CPR / 64;
+#pragma unroll
+    for (int i0 = 0; i0 < INSTR / 4; ++i0) {
+      const int i = i0 * 4 + wave, slot = i * 64 + lane;
+      const int r = slot / CPR, pos = slot % CPR, c = pos ^ swz<D, MODE>(r);
+      const int mn = min(mn0 + c * 8, MN - 8);
+      __builtin_amdgcn_global_load_lds((const void*)gemm_elem(op, mn, (int64_t)k0 + r), (lds_void*)(tile + i * 512),
+                                       16, 0, 0);
+    }
+  }
+}
+
+// Operand fragment for MFMA step ks (k = 16 ks .. 16 ks + 15 of the tile) and
+// the 32-row block mb of the operand's 128 M (or N) rows, in the k order of a
+// P fragment (see the file comment).
+template <int MODE>
+__device__ __forceinline__ bf16x8 gemm_frag(const bf16* tile, int kmajor, int ks, int mb, int lane) {
+  if (kmajor) {
+    const int row = mb * 32 + (lane & 31), half = lane >> 5;
+    const bf16* p0 = tile + tile_off<64, MODE>(row, 2 * ks) + 4 * half;
+    const bf16* p1 = tile + tile_off<64, MODE>(row, 2 * ks + 1) + 4 * half;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p0);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  return tile_tr_frag<128, MODE>(tile, 16 * ks, mb * 32, lane);
+}
+
+// 4 waves, 128 x 128 tile of C per workgroup, each wave 64 x 64 (2 x 2 MFMA
+// tiles of 32 x 32), K in steps of 64, LDS double-buffered (64 KiB).
+template <typename CT>
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams<CT> p) {
+  constexpr int MODE = kSwzAll;
+  __shared__ __attribute__((aligned(1024))) bf16 sA[2][128 * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sB[2][128 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * 128, n0 = blockIdx.y * 128;
+  const int wm = (wave & 1) * 2, wn = (wave >> 1) * 2;  // this wave's 32-row blocks of M and of N
+  const int nk = p.K / 64;
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+
+  gemm_load_tile<MODE>(sA[0], p.a, m0, p.M, 0, wave, lane);
+  gemm_load_tile<MODE>(sB[0], p.b, n0, p.N, 0, wave, lane);
+  wait_vm();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      gemm_load_tile<MODE>(sA[cur ^ 1], p.a, m0, p.M, (kt + 1) * 64, wave, lane);
+      gemm_load_tile<MODE>(sB[cur ^ 1], p.b, n0, p.N, (kt + 1) * 64, wave, lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = gemm_frag<MODE>(sA[cur], p.a.kmajor, ks, wm + i, lane);
+        bfr[i] = gemm_frag<MODE>(sB[cur], p.b.kmajor, ks, wn + i, lane);
+      }
+      // C^T tiles: lane = m (column of C^T), registers = n
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma32(acc[i][j], bfr[j], af[i]);
+    }
+    wait_vm();
+    __syncthreads();
+  }
+
+  const int half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + (wm + i) * 32 + (lane & 31);
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + (wn + j) * 32 + 8 * g + 4 * half;  // registers 4g .. 4g+3: n .. n+3
+        if (n >= p.N) continue;
+        CT* dst = p.c.p + (n / p.c.blk) * p.c.blk_stride + (int64_t)m * p.c.ldc + (n % p.c.blk);
+        floatx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+        if constexpr (std::is_same<CT, float>::value) {
+          if (p.accumulate) {
+            const floatx4 old = *reinterpret_cast<const floatx4*>(dst);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = old[e] + v[e];
+          }
+          *reinterpret_cast<floatx4*>(dst) = v;
+        } else {
+          *reinterpret_cast<bf16x4*>(dst) = to_out4(v, bf16());
+        }
+      }
+  }
+}
+
+}  // namespace upipe

@@ -27,6 +27,7 @@
 #include "attn_bwd.hpp"
 #include "attn_fwd.hpp"
 #include "copy_kernels.hpp"
+#include "gemm_bf16.hpp"
 
 namespace upipe {
 namespace {
@@ -71,8 +72,10 @@ int validate(int64_t S, int Hq, int Hkv, int d, int hc, int causal, int dtype, P
   const size_t es = dtype == UPIPE_BF16 ? 2 : 4;
   if ((uint64_t)S * (uint64_t)d >= (1ull << 31))
     return fail(UPIPE_EUNSUPPORTED, "S*d must be < 2^31 (S=%lld, d=%d)", (long long)S, d);
-  if ((uint64_t)S * (uint64_t)std::max(Hq, Hkv) * (uint64_t)d * es / 16 >= (1ull << 32))
-    return fail(UPIPE_EUNSUPPORTED, "tensor too large for 32-bit vector indexing");
+  // Copy kernels index tokens with 64 bits; this only keeps byte sizes far
+  // from size_t overflow (2^48 bytes = 256 TiB per tensor).
+  if ((uint64_t)S * (uint64_t)std::max(Hq, Hkv) * (uint64_t)d * es >= (1ull << 48))
+    return fail(UPIPE_EUNSUPPORTED, "tensor larger than 2^48 bytes");
   pr->S = S;
   pr->Hq = Hq;
   pr->Hkv = Hkv;
@@ -163,9 +166,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // ---------------------------------------------------------------------------
 // Optional per-kernel timing with HIP events on the launch stream.
 // ---------------------------------------------------------------------------
-enum KernelId { K_PACK = 0, K_UNPACK, K_FWD, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_COUNT };
+enum KernelId { K_PACK = 0, K_UNPACK, K_FWD, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_GEMM, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"pack_heads", "unpack_heads", "attn_fwd", "bwd_pre", "attn_bwd_dkdv",
-                                           "attn_bwd_dq"};
+                                           "attn_bwd_dq", "gemm_bf16"};
 struct Profiler {
   std::atomic<bool> on{false};
   struct Rec {
@@ -396,6 +399,150 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
   return UPIPE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 GEMM (gemm_bf16.hpp): argument checks and launch.
+// ---------------------------------------------------------------------------
+constexpr int64_t kUnblocked = (int64_t)1 << 62;  // a contiguous index that never wraps
+
+GemmOperand operand(const void* p, int64_t ld, int kmajor, int64_t blk = kUnblocked, int64_t blk_stride = 0) {
+  GemmOperand o;
+  o.p = reinterpret_cast<const bf16*>(p);
+  o.ld = ld;
+  o.blk = blk;
+  o.blk_stride = blk_stride;
+  o.kmajor = kmajor;
+  return o;
+}
+
+int check_operand(const char* name, const GemmOperand& o, int MN, int K) {
+  if (!o.p) return fail(UPIPE_EINVAL, "%s is NULL", name);
+  if ((uintptr_t)o.p % 16) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", name);
+  if (o.ld < 1 || o.ld % 8) return fail(UPIPE_EINVAL, "%s: leading dimension %lld is not a positive multiple of 8",
+                                        name, (long long)o.ld);
+  if (o.blk < 8 || o.blk % 8 || (o.blk < kUnblocked && (o.blk_stride < 0 || o.blk_stride % 8)))
+    return fail(UPIPE_EINVAL, "%s: block length must be a multiple of 8 and the block stride of 8", name);
+  if (!o.kmajor && MN % 8) return fail(UPIPE_EINVAL, "%s: an M/N-contiguous operand needs M or N a multiple of 8", name);
+  (void)K;
+  return UPIPE_OK;
+}
+
+template <typename CT>
+int gemm(const GemmOperand& a, const GemmOperand& b, const GemmOut<CT>& c, int M, int N, int K, int accumulate,
+         hipStream_t st) {
+  GemmParams<CT> p;
+  p.a = a;
+  p.b = b;
+  p.c = c;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.accumulate = accumulate;
+  hipLaunchKernelGGL((gemm_bf16_kernel<CT>), dim3((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128)),
+                     dim3(256), 0, st, p);
+  return check_launch("gemm");
+}
+
+// ---------------------------------------------------------------------------
+// Attention block (projections around the chunked attention), forward.
+// Pool: the chunk's q and attention output rows (head-major), its kv heads'
+// k rows, their v rows token-major as the projection writes them and again
+// transposed for the forward kernel. Every chunk reuses the same offsets.
+// ---------------------------------------------------------------------------
+struct BlockPool {
+  size_t q, o, k, vtmp, vt, total;
+};
+BlockPool block_pool(const Problem& pr) {
+  const size_t U = (size_t)pr.S * pr.d * pr.es;
+  BlockPool p;
+  size_t off = 0;
+  p.q = off; off += align_up(pr.hc * U);
+  p.o = off; off += align_up(pr.hc * U);
+  p.k = off; off += align_up(pr.nkv * U);
+  p.vtmp = off; off += align_up(pr.nkv * U);
+  p.vt = off; off += align_up(pr.nkv * vt_bytes(pr));
+  p.total = off;
+  return p;
+}
+
+int validate_block(int64_t S, int Dm, int Hq, int Hkv, int d, int hc, int causal, Problem* pr) {
+  if (int rc = validate(S, Hq, Hkv, d, hc, causal, UPIPE_BF16, pr)) return rc;
+  if (Dm < 64 || Dm % 64) return fail(UPIPE_EUNSUPPORTED, "model dim Dm (%d) must be a positive multiple of 64", Dm);
+  if ((uint64_t)S * (uint64_t)Dm * 4 >= (1ull << 48)) return fail(UPIPE_EUNSUPPORTED, "x larger than 2^48 bytes");
+  return UPIPE_OK;
+}
+
+template <int D>
+int run_block_fwd(const Problem& pr, int Dm, const void* x, const void* wq, const void* wk, const void* wv,
+                  const void* wo, float* y, void* out, float* lse, char* ws, hipStream_t st) {
+  const BlockPool pool = block_pool(pr);
+  const int S = (int)pr.S;
+  bf16* Qc = reinterpret_cast<bf16*>(ws + pool.q);
+  bf16* Oc = reinterpret_cast<bf16*>(ws + pool.o);
+  bf16* Kc = reinterpret_cast<bf16*>(ws + pool.k);
+  bf16* Vtmp = reinterpret_cast<bf16*>(ws + pool.vtmp);
+  bf16* Vt = reinterpret_cast<bf16*>(ws + pool.vt);
+  const int n_qtiles = (S + 127) / 128;
+  const float scale = 1.0f / std::sqrt((float)D);
+  const int64_t SD = (int64_t)S * D;
+  const GemmOperand xa = operand(x, Dm, 1);  // [S][Dm], K = Dm contiguous
+  for (const Chunk& c : plan(pr)) {
+    if (c.load_kv) {
+      // k of the chunk's kv heads, head-major [nkv][S][D]; v token-major [S][nkv*D]
+      const GemmOperand wkb = operand(reinterpret_cast<const bf16*>(wk) + (int64_t)c.kv_head0 * D * Dm, Dm, 1);
+      const GemmOperand wvb = operand(reinterpret_cast<const bf16*>(wv) + (int64_t)c.kv_head0 * D * Dm, Dm, 1);
+      GemmOut<bf16> kout = {Kc, D, D, SD};
+      GemmOut<bf16> vout = {Vtmp, (int64_t)c.n_kv * D, kUnblocked, 0};
+      timed(K_GEMM, st, [&] { (void)gemm(xa, wkb, kout, S, c.n_kv * D, Dm, 0, st); });
+      timed(K_GEMM, st, [&] { (void)gemm(xa, wvb, vout, S, c.n_kv * D, Dm, 0, st); });
+      timed(K_PACK, st, [&] {
+        hipLaunchKernelGGL((pack_vt_kernel<D>), dim3((unsigned)(vt_len(pr) / 64), c.n_kv), dim3(256), 0, st, Vtmp,
+                           Vt, S, (int)vt_len(pr), c.n_kv, 0);
+      });
+    }
+    const GemmOperand wqb = operand(reinterpret_cast<const bf16*>(wq) + (int64_t)c.q_head0 * D * Dm, Dm, 1);
+    GemmOut<bf16> qout = {Qc, D, D, SD};
+    timed(K_GEMM, st, [&] { (void)gemm(xa, wqb, qout, S, pr.hc * D, Dm, 0, st); });
+    FwdParams<bf16> fp;
+    fp.Sp = (int)vt_len(pr);
+    fp.q = Qc;
+    fp.k = Kc;
+    fp.v = Vt;
+    fp.o = Oc;
+    fp.o_lo = nullptr;
+    fp.H = pr.Hq;
+    fp.lse = lse + (size_t)c.q_head0 * S;
+    fp.S = S;
+    fp.hc = pr.hc;
+    fp.heads_per_kv = pr.heads_per_kv;
+    fp.n_qtiles = n_qtiles;
+    fp.causal = pr.causal;
+    fp.doc_off = nullptr;
+    fp.n_docs = 0;
+    fp.scale_log2 = scale * kLog2e;
+    timed(K_FWD, st, [&] {
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, fp);
+    });
+    if (out) {
+      const size_t nq = (size_t)S * pr.hc * (D / 8);
+      timed(K_UNPACK, st, [&] {
+        hipLaunchKernelGGL(unpack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)Oc, (uint4*)out,
+                           S, pr.Hq, c.q_head0, pr.hc, D / 8);
+      });
+    }
+    // y (+)= o_h Wo_h^T one head at a time, in head order, so y's fp32 sums
+    // do not depend on head_chunk
+    for (int hl = 0; hl < pr.hc; ++hl) {
+      const int h = c.q_head0 + hl;
+      const GemmOperand oa = operand(Oc + (int64_t)hl * SD, D, 1);
+      const GemmOperand wob = operand(reinterpret_cast<const bf16*>(wo) + (int64_t)h * D, (int64_t)pr.Hq * D, 1);
+      GemmOut<float> yout = {y, Dm, kUnblocked, 0};
+      timed(K_GEMM, st, [&] { (void)gemm(oa, wob, yout, S, Dm, D, h > 0, st); });
+    }
+    if (int rc = check_launch("attention block chunk")) return rc;
+  }
+  return UPIPE_OK;
+}
+
 }  // namespace
 }  // namespace upipe
 
@@ -415,6 +562,30 @@ size_t upipe_attn_bwd_workspace_bytes(int64_t S, int Hq, int Hkv, int d, int hea
   if (validate(S, Hq, Hkv, d, head_chunk, 1, dtype, &pr) != UPIPE_OK) return 0;
   g_error.clear();
   return bwd_pool(pr).total;
+}
+
+size_t upipe_attn_workspace_bytes(int64_t S, int Hq, int Hkv, int d, int head_chunk, int dtype) {
+  Problem pr;
+  if (validate(S, Hq, Hkv, d, head_chunk, 1, dtype, &pr) != UPIPE_OK) return 0;
+  g_error.clear();
+  return std::max(fwd_pool(pr).total, bwd_pool(pr).total);
+}
+
+int upipe_attn_pick_head_chunk(int64_t S, int Hq, int Hkv, int d, int dtype, size_t budget_bytes) {
+  Problem pr;
+  if (int rc = validate(S, Hq, Hkv, d, 1, 1, dtype, &pr)) return rc;
+  int best = 0;
+  size_t need1 = 0;
+  for (int hc = 1; hc <= Hq; ++hc) {
+    if (validate(S, Hq, Hkv, d, hc, 1, dtype, &pr) != UPIPE_OK) continue;  // not a valid chunk size
+    const size_t need = std::max(fwd_pool(pr).total, bwd_pool(pr).total);
+    if (hc == 1) need1 = need;
+    if (need <= budget_bytes) best = hc;  // pools grow strictly with hc: the last fit is the largest
+  }
+  if (!best)
+    return fail(UPIPE_EWORKSPACE, "even head_chunk 1 needs %zu workspace bytes, budget %zu", need1, budget_bytes);
+  g_error.clear();
+  return best;
 }
 
 }  // extern "C"
@@ -526,6 +697,67 @@ int upipe_attn_bwd_docs(const void* q, const void* k, const void* v, const void*
   if (!doc_offsets && !n_docs) return fail(UPIPE_EINVAL, "doc_offsets is NULL");
   return bwd_entry(q, k, v, out, out_lo, dout, lse, dq, dk, dv, S, Hq, Hkv, d, head_chunk, causal, doc_offsets,
                    n_docs, dtype, workspace, workspace_bytes, stream);
+}
+
+int upipe_gemm_bf16(const void* a, int64_t lda, int64_t a_blk, int64_t a_blk_stride, int a_kmajor, const void* b,
+                    int64_t ldb, int64_t b_blk, int64_t b_blk_stride, int b_kmajor, void* c, int64_t ldc,
+                    int64_t c_blk, int64_t c_blk_stride, int c_dtype, int accumulate, int M, int N, int K,
+                    void* stream) {
+  if (M < 1 || N < 1 || K < 1) return fail(UPIPE_EINVAL, "M, N, K must be >= 1 (got %d, %d, %d)", M, N, K);
+  if (K % 64) return fail(UPIPE_EUNSUPPORTED, "K (%d) must be a multiple of 64", K);
+  if (N % 8) return fail(UPIPE_EUNSUPPORTED, "N (%d) must be a multiple of 8", N);
+  if (c_dtype != UPIPE_BF16 && c_dtype != UPIPE_FP32) return fail(UPIPE_EUNSUPPORTED, "unsupported C dtype %d", c_dtype);
+  if (accumulate && c_dtype != UPIPE_FP32) return fail(UPIPE_EINVAL, "accumulate needs an fp32 C");
+  const GemmOperand ao = operand(a, lda, a_kmajor != 0, a_blk > 0 ? a_blk : kUnblocked, a_blk_stride);
+  const GemmOperand bo = operand(b, ldb, b_kmajor != 0, b_blk > 0 ? b_blk : kUnblocked, b_blk_stride);
+  if (int rc = check_operand("a", ao, M, K)) return rc;
+  if (int rc = check_operand("b", bo, N, K)) return rc;
+  if (!c) return fail(UPIPE_EINVAL, "c is NULL");
+  if ((uintptr_t)c % 16) return fail(UPIPE_EINVAL, "c is not 16-byte aligned");
+  const int64_t cb = c_blk > 0 ? c_blk : kUnblocked;
+  if (ldc < 1 || ldc % 8 || cb % 8 || (cb < kUnblocked && c_blk_stride % 8))
+    return fail(UPIPE_EINVAL, "c: ldc, block length and block stride must be multiples of 8");
+  g_error.clear();
+  (void)hipGetLastError();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int rc;
+  timed(K_GEMM, st, [&] {
+    if (c_dtype == UPIPE_FP32)
+      rc = gemm(ao, bo, GemmOut<float>{reinterpret_cast<float*>(c), ldc, cb, c_blk_stride}, M, N, K, accumulate, st);
+    else
+      rc = gemm(ao, bo, GemmOut<bf16>{reinterpret_cast<bf16*>(c), ldc, cb, c_blk_stride}, M, N, K, 0, st);
+  });
+  return rc;
+}
+
+size_t upipe_attn_block_fwd_workspace_bytes(int64_t S, int Dm, int Hq, int Hkv, int d, int head_chunk) {
+  Problem pr;
+  if (validate_block(S, Dm, Hq, Hkv, d, head_chunk, 1, &pr) != UPIPE_OK) return 0;
+  g_error.clear();
+  return block_pool(pr).total;
+}
+
+int upipe_attn_block_fwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wo, float* y,
+                         void* out, float* lse, int64_t S, int Dm, int Hq, int Hkv, int d, int head_chunk,
+                         int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  Problem pr;
+  if (int rc = validate_block(S, Dm, Hq, Hkv, d, head_chunk, causal, &pr)) return rc;
+  const void* ptrs[] = {x, wq, wk, wv, wo, y, lse, workspace};
+  const char* names[] = {"x", "wq", "wk", "wv", "wo", "y", "lse", "workspace"};
+  for (int i = 0; i < 8; ++i) {
+    if (!ptrs[i]) return fail(UPIPE_EINVAL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  if (out && !aligned16(out)) return fail(UPIPE_EINVAL, "out is not 16-byte aligned");
+  const size_t need = block_pool(pr).total;
+  if (workspace_bytes < need)
+    return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  g_error.clear();
+  (void)hipGetLastError();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (d == 128) return run_block_fwd<128>(pr, Dm, x, wq, wk, wv, wo, y, out, lse, ws, st);
+  return run_block_fwd<64>(pr, Dm, x, wq, wk, wv, wo, y, out, lse, ws, st);
 }
 
 int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks, int32_t* q_head0, int32_t* kv_head0,

@@ -172,3 +172,17 @@ def tail_keys(S: int, n: int, window: int, seed: int) -> np.ndarray:
     if span > 2:
         keys.update(int(x) for x in rng.choice(np.arange(lo, S), size=min(n, span), replace=False))
     return np.array(sorted(keys), dtype=np.int64)
+
+
+def make_block_inputs(S: int, Dm: int, Hq: int, Hkv: int, d: int, seed: int, device="cpu"):
+    """Inputs of the attention block: x [S, Dm] ~ N(0,1) and torch-Linear
+    weights wq [Hq*d, Dm], wk, wv [Hkv*d, Dm] ~ N(0, 1/Dm), wo [Dm, Hq*d] ~
+    N(0, 1/(Hq*d)) (unit-variance projections), all rounded to bf16.
+    Seeds: x = seed, wq = seed+1, wk = seed+2, wv = seed+3, wo = seed+4."""
+    dt = torch.bfloat16
+    x = _normal((S, Dm), seed, device, dt)
+    wq = _normal((Hq * d, Dm), seed + 1, device, torch.float32).mul_(1 / math.sqrt(Dm)).to(dt)
+    wk = _normal((Hkv * d, Dm), seed + 2, device, torch.float32).mul_(1 / math.sqrt(Dm)).to(dt)
+    wv = _normal((Hkv * d, Dm), seed + 3, device, torch.float32).mul_(1 / math.sqrt(Dm)).to(dt)
+    wo = _normal((Dm, Hq * d), seed + 4, device, torch.float32).mul_(1 / math.sqrt(Hq * d)).to(dt)
+    return x, wq, wk, wv, wo

@@ -10,6 +10,9 @@ from .attention import (  # noqa: F401
     attention_backward,
     forward_rows,
     backward_rows_dq,
+    rows_forward_dq,
     backward_cols_dkdv,
+    cols_rows_needed,
     kv_head_of,
 )
+from .block import attention_block_forward, attention_block_rows, round_bf16  # noqa: F401,E402

@@ -72,12 +72,16 @@ __all__ = [
     "attention_backward",
     "forward_rows",
     "backward_rows_dq",
+    "rows_forward_dq",
     "backward_cols_dkdv",
+    "cols_rows_needed",
     "document_bounds",
 ]
 
-# Upper bound on the number of float64 score elements held at once (512 MiB).
-_SCORE_BUDGET = 1 << 26
+# Upper bound on the number of float64 score elements held at once (1 GiB).
+# Batching only: each batch of rows streams K and V once, so larger batches
+# read them fewer times; the numbers do not depend on it.
+_SCORE_BUDGET = 1 << 27
 
 
 def _f64(x) -> np.ndarray:
@@ -286,14 +290,69 @@ def backward_rows_dq(q_rows, k, v, dout_rows, rows, causal: bool = True, doc_off
     return dq
 
 
-def backward_cols_dkdv(q, k, v, dout, cols, causal: bool = True, doc_offsets=None):
+def rows_forward_dq(q_rows, k, v, dout_rows, rows, causal: bool = True, doc_offsets=None):
+    """Exact O, LSE and dQ at selected query rows from one pass over each
+    row's scores: the forward's softmax rows P and O = P V, then D = <dO, O>,
+    dP = dO V^T, dS = P (dP - D) and dQ = tau dS K on the same P. O(S*d) work
+    per row; the same numbers as :func:`forward_rows` and
+    :func:`backward_rows_dq`, at two thirds of their combined cost.
+
+    Returns (out_rows [R,Hq,d], lse_rows [Hq,R], dq_rows [R,Hq,d]) in float64,
+    in ``rows`` order.
+    """
+    q_rows, k, v, dout_rows = _f64(q_rows), _f64(k), _f64(v), _f64(dout_rows)
+    rows = np.asarray(rows, dtype=np.int64)
+    S, Hkv, d = k.shape
+    Hq = q_rows.shape[1]
+    G = Hq // Hkv
+    tau = 1.0 / math.sqrt(d)
+    bounds = _bounds(doc_offsets, S)
+    out = np.zeros((len(rows), Hq, d))
+    lse = np.zeros((Hq, len(rows)))
+    dq = np.zeros((len(rows), Hq, d))
+    for sel in _row_batches(rows, S, causal, G):
+        r = rows[sel]
+        n_cols = int(r.max()) + 1 if causal else S
+        mask = _look_back_mask(r, n_cols, causal, bounds)
+        for g in range(Hkv):
+            hs = [h for h in range(Hq) if kv_head_of(h, Hq, Hkv) == g]
+            k_g, v_g = k[:n_cols, g, :], v[:n_cols, g, :]
+            s = _group_scores(q_rows[sel][:, hs, :], k_g, tau, mask)
+            p, lse_blk = _softmax_rows(s)
+            o = _rows_matmul(p, v_g)
+            out[np.ix_(sel, hs)] = o
+            lse[np.ix_(hs, sel)] = lse_blk.T
+            do_blk = dout_rows[sel][:, hs, :]
+            D = (do_blk * o).sum(axis=-1)
+            ds = p * (_rows_matmul(do_blk, v_g.T) - D[..., None])
+            dq[np.ix_(sel, hs)] = tau * _rows_matmul(ds, k_g)
+    return out, lse, dq
+
+
+def cols_rows_needed(cols, S: int, causal: bool = True, doc_offsets=None) -> np.ndarray:
+    """The query rows whose softmax rows reach any of the keys ``cols``: from
+    the first key on when causal (from 0 otherwise), narrowed to the keys'
+    documents when the sequence is packed. Sorted positions."""
+    cols = np.asarray(cols, dtype=np.int64)
+    bounds = _bounds(doc_offsets, S)
+    first = int(cols.min()) if causal else 0
+    end = S
+    if bounds is not None:
+        first = max(first, int(bounds[0][cols].min()))
+        end = int(bounds[1][cols].max()) + 1
+    return np.arange(first, end)
+
+
+def backward_cols_dkdv(q, k, v, dout, cols, causal: bool = True, doc_offsets=None, row_stats=None):
     """Exact dK and dV at selected key rows, from the inputs alone.
 
     Key j collects from every row i with j in A(i): i >= j when causal, every
     row otherwise, and with packed documents only rows of j's own document.
     Each such row's LSE and O come from :func:`forward_rows`, so the cost is
     O(|rows| * S * d), which is small when the keys lie near the end of a
-    causal sequence or in short documents.
+    causal sequence or in short documents. ``row_stats`` may hand in that
+    step's result, (out [R,Hq,d], lse [Hq,R]) of :func:`forward_rows` at the
+    rows :func:`cols_rows_needed` names, computed elsewhere (e.g. in pieces).
     Returns (dk_cols [C,Hkv,d], dv_cols [C,Hkv,d]).
     """
     k, v = _f64(k), _f64(v)
@@ -302,14 +361,13 @@ def backward_cols_dkdv(q, k, v, dout, cols, causal: bool = True, doc_offsets=Non
     Hq = q.shape[1]
     tau = 1.0 / math.sqrt(d)
     bounds = _bounds(doc_offsets, S)
-    first = int(cols.min()) if causal else 0
-    end = S
-    if bounds is not None:
-        first = max(first, int(bounds[0][cols].min()))
-        end = int(bounds[1][cols].max()) + 1
-    need = np.arange(first, end)
+    need = cols_rows_needed(cols, S, causal, doc_offsets)
+    first, end = int(need[0]), int(need[-1]) + 1
     q_need, do_need = _f64(q[first:end]), _f64(dout[first:end])
-    o_need, lse_need = forward_rows(q_need, k, v, need, causal, doc_offsets)
+    if row_stats is None:
+        o_need, lse_need = forward_rows(q_need, k, v, need, causal, doc_offsets)
+    else:
+        o_need, lse_need = _f64(row_stats[0]), _f64(row_stats[1])
     dk = np.zeros((len(cols), Hkv, d))
     dv = np.zeros((len(cols), Hkv, d))
     n_rows = len(need)

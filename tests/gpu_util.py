@@ -14,6 +14,14 @@ import long_context_attention_upipe_amd as up
 TOL = {"bf16": (2e-2, 5e-3), "fp32": (2e-2, 1e-4)}
 
 
+def grad_scale(w):
+    """Factor that brings gradients back to unit dO scale: sqrt(S) for the
+    workloads whose dO is drawn as N(0,1)/sqrt(S), else 1."""
+    import math
+
+    return math.sqrt(w.S) if w.dout_scaled else 1.0
+
+
 def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
@@ -44,15 +52,52 @@ def errors(got, ref):
     return max_abs, rel
 
 
-def assert_close(name, got, ref, dtype, rel_only=False):
+def assert_close(name, got, ref, dtype, rel_only=False, grad_scale=1.0, per_item=False):
+    """max |err| and relative Frobenius error of a tensor against the oracle.
+
+    grad_scale: gradients are linear in dO, so for workloads whose dO is drawn
+    at a reduced scale (N(0,1)/sqrt(S)) both sides are multiplied back to unit
+    dO scale (grad_scale = sqrt(S)) before the max-abs bound is applied, as
+    |err| <= 2e-2 * max(|ref|, 1) per element.
+    per_item: also bound the error of every item along axis 0 (a sampled row
+    or key): ||err_i|| <= PER_ITEM_FACTOR * rel_tol * max(||ref_i||, rms_i
+    ||ref_i||), so one wrong row or key fails even when the tensor-wide norm
+    would absorb it."""
     max_abs_tol, rel_tol = TOL[dtype]
     if rel_only:
         max_abs_tol = float("inf")
     assert np.isfinite(got).all(), f"{name}: non-finite values"
-    max_abs, rel = errors(got, ref)
-    print(f"    {name:4s} max_abs={max_abs:.3e} rel_fro={rel:.3e}", flush=True)
+    max_abs, rel = errors(got * grad_scale, ref * grad_scale)
+    msg = f"    {name:4s} max_abs={max_abs:.3e}" + (f" (x{grad_scale:.4g}, unit dO)" if grad_scale != 1.0 else "") \
+        + f" rel_fro={rel:.3e}"
+    if grad_scale != 1.0:
+        # At unit dO scale gradient entries reach ~10 (a key's dV sums dO over
+        # the rows that see it), where bf16's own half-ulp, 2^-8 |x|, exceeds
+        # 2e-2: the bound is absolute for |ref| <= 1 and relative above.
+        g, r_ = got * grad_scale, ref * grad_scale
+        max_abs = float((np.abs(g - r_) / np.maximum(np.abs(r_), 1.0)).max()) if ref.size else 0.0
+        msg += f" max_err/max(|ref|,1)={max_abs:.3e}"
+    worst = None
+    if per_item and ref.shape[0] > 1:
+        n = ref.shape[0]
+        err_i = np.linalg.norm((got - ref).reshape(n, -1), axis=1)
+        ref_i = np.linalg.norm(ref.reshape(n, -1), axis=1)
+        floor = float(np.sqrt(np.mean(ref_i ** 2)))
+        ratio = err_i / np.maximum(ref_i, floor) if floor > 0 else err_i
+        worst = (float(ratio.max()), int(ratio.argmax()))
+        msg += f" worst_item={worst[0]:.3e}@{worst[1]}"
+    print(msg, flush=True)
     assert max_abs <= max_abs_tol and rel <= rel_tol, \
         f"{name}: max_abs={max_abs:.3e} (tol {max_abs_tol}) rel_fro={rel:.3e} (tol {rel_tol})"
+    if worst is not None:
+        assert worst[0] <= PER_ITEM_FACTOR * rel_tol, \
+            f"{name}: item {worst[1]} off by {worst[0]:.3e} of its norm (tol {PER_ITEM_FACTOR * rel_tol})"
+
+
+# One item (row or key) may be worse than the tensor as a whole, which averages
+# many items; 4x the tensor-wide relative bound still fails any item whose
+# value is wrong rather than rounded.
+PER_ITEM_FACTOR = 4.0
 
 
 def bit_equal(a, b):
@@ -60,26 +105,56 @@ def bit_equal(a, b):
                        b.view(torch.uint8) if b.dtype != torch.float32 else b.view(torch.int32))
 
 
-def oracle_parallel(fn, parts, label):
-    """[fn(p) for p in parts], evaluated on a thread pool with single-threaded
-    BLAS: the oracle's per-row work is numpy elementwise passes, which release
-    the GIL but run on one core each. Prints a progress line as parts finish."""
-    from concurrent.futures import ThreadPoolExecutor, as_completed
+class OracleJobs:
+    """Oracle work on a host thread pool that runs while the GPU computes.
 
-    from threadpoolctl import threadpool_limits
+    Every BLAS call is held to ONE thread while the pool runs: OpenBLAS
+    (pthreads build) called concurrently from several threads, each running
+    its own multi-threaded GEMMs, returned wrong products on the GPU machine's
+    host (a full-tensor oracle run per head in 4 threads x 4 BLAS threads
+    differed from the per-row oracle on 13,196 of 131,072 rows, on different
+    rows from run to run), while single-threaded calls from many threads gave
+    the same numbers as sequential runs. Parallelism comes from splitting the
+    work into parts instead (the per-row work is numpy elementwise passes
+    plus matrix products, which release the GIL). map() submits and returns
+    at once; gather() blocks, printing a progress line as parts finish."""
 
-    workers = max(1, min(16, os.cpu_count() or 1, len(parts)))
-    results = [None] * len(parts)
-    t0 = last = time.perf_counter()
-    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
-        futures = {ex.submit(fn, p): i for i, p in enumerate(parts)}
+    def __init__(self, workers=None):
+        from concurrent.futures import ThreadPoolExecutor
+
+        from threadpoolctl import threadpool_limits
+
+        cores = max(1, min(16, os.cpu_count() or 1))
+        self.workers = workers or max(1, cores - 1)  # one core left for the GPU's host thread
+        self._limits = threadpool_limits(1)
+        self._ex = ThreadPoolExecutor(self.workers)
+        self._t0 = time.perf_counter()
+
+    def map(self, fn, parts, label):
+        return label, [self._ex.submit(fn, p) for p in parts]
+
+    def gather(self, job):
+        from concurrent.futures import as_completed
+
+        label, futures = job
+        last = time.perf_counter()
         for n_done, fut in enumerate(as_completed(futures), 1):
-            results[futures[fut]] = fut.result()
+            fut.result()
             now = time.perf_counter()
-            if now - last > 20 or n_done == len(parts):
-                print(f"   oracle {label}: {n_done}/{len(parts)} parts, {now - t0:.0f}s", flush=True)
+            if now - last > 20 or n_done == len(futures):
+                print(f"   oracle {label}: {n_done}/{len(futures)} parts, {now - self._t0:.0f}s", flush=True)
                 last = now
-    return results
+        return [f.result() for f in futures]
+
+    def close(self):
+        self._ex.shutdown(wait=True, cancel_futures=True)
+        self._limits.restore_original_limits()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
 
 
 def interleaved_parts(n, n_parts):

@@ -204,10 +204,25 @@ def pin_sampled_functions(mod, S=53, Hq=4, Hkv=1, d=8):
             np.testing.assert_allclose(l_r, lse[:, rows], rtol=1e-12, atol=1e-13)
             dq_r = mod.backward_rows_dq(q[rows], k, v, do[rows], rows, causal=causal)
             np.testing.assert_allclose(dq_r, dq[rows], rtol=1e-11, atol=1e-12)
+            # the single-pass row function: the same O, LSE and dQ
+            o_f, l_f, dq_f = mod.rows_forward_dq(q[rows], k, v, do[rows], rows, causal=causal)
+            np.testing.assert_allclose(o_f, out[rows], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(l_f, lse[:, rows], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(dq_f, dq[rows], rtol=1e-11, atol=1e-12)
         cols = np.array([52, 40, 45, 3]) if not causal else np.array([52, 40, 45])
         dk_c, dv_c = mod.backward_cols_dkdv(q, k, v, do, cols, causal=causal)
         np.testing.assert_allclose(dk_c, dk[cols], rtol=1e-11, atol=1e-12)
         np.testing.assert_allclose(dv_c, dv[cols], rtol=1e-11, atol=1e-12)
+        # the rows the keys need, their forward computed in two pieces and handed in
+        need = mod.cols_rows_needed(cols, S, causal=causal)
+        assert list(need) == (list(range(40, S)) if causal else list(range(S)))
+        h = len(need) // 2
+        o1, l1 = mod.forward_rows(q[need[:h]], k, v, need[:h], causal=causal)
+        o2, l2 = mod.forward_rows(q[need[h:]], k, v, need[h:], causal=causal)
+        stats = (np.concatenate([o1, o2]), np.concatenate([l1, l2], axis=1))
+        dk_s, dv_s = mod.backward_cols_dkdv(q, k, v, do, cols, causal=causal, row_stats=stats)
+        np.testing.assert_allclose(dk_s, dk[cols], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dv_s, dv[cols], rtol=1e-11, atol=1e-12)
 
 
 # --- packed documents -------------------------------------------------------
@@ -322,10 +337,18 @@ def pin_docs_sampled_functions(mod, S=41, Hq=4, Hkv=2, d=8):
         np.testing.assert_allclose(l_r, lse[:, rows], rtol=1e-12, atol=1e-13)
         dq_r = mod.backward_rows_dq(q[rows], k, v, do[rows], rows, causal=causal, doc_offsets=DOC_OFFSETS)
         np.testing.assert_allclose(dq_r, dq[rows], rtol=1e-11, atol=1e-12)
+        o_f, l_f, dq_f = mod.rows_forward_dq(q[rows], k, v, do[rows], rows, causal=causal,
+                                             doc_offsets=DOC_OFFSETS)
+        np.testing.assert_allclose(o_f, out[rows], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(l_f, lse[:, rows], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dq_f, dq[rows], rtol=1e-11, atol=1e-12)
         for cols in (np.array([40, 31, 25, 12]), np.array([0, 5]), np.array([29, 24])):
             dk_c, dv_c = mod.backward_cols_dkdv(q, k, v, do, cols, causal=causal, doc_offsets=DOC_OFFSETS)
             np.testing.assert_allclose(dk_c, dk[cols], rtol=1e-11, atol=1e-12)
             np.testing.assert_allclose(dv_c, dv[cols], rtol=1e-11, atol=1e-12)
+        # keys 29 and 24 sit in the document [24, 30): only its rows are needed
+        need = mod.cols_rows_needed(np.array([29, 24]), S, causal=causal, doc_offsets=DOC_OFFSETS)
+        assert list(need) == list(range(24, 30))
 
 
 ALL_PINS = [
@@ -356,5 +379,109 @@ def failing_pins(mod):
             with np.errstate(all="ignore"):
                 pin(mod)
         except Exception:  # noqa: BLE001 - a crash is a failed pin too
+            bad.append(pin.__name__)
+    return bad
+
+
+# --- the attention block (projections around the chunked attention) ---------
+
+def _bf16_values(shape, seed, scale=1.0):
+    """Random values that bf16 holds exactly (a bf16 tensor's contents)."""
+    t = torch.tensor(_rand(shape, seed) * scale).to(torch.bfloat16).to(torch.float64)
+    return t.numpy()
+
+
+def pin_round_bf16(bmod, amod=None):
+    """round_bf16 against torch's float32 -> bfloat16 conversion (round to
+    nearest even), on random values, exact ties and values bf16 holds."""
+    x = np.concatenate([_rand(4096, 61) * 10.0 ** np.arange(-3, 5).repeat(512),
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130, 0.0, -0.0])])
+    ref = torch.tensor(x).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(bmod.round_bf16(x), ref)
+    v = _bf16_values(1000, 62)
+    np.testing.assert_array_equal(bmod.round_bf16(v), v)
+
+
+def pin_block_vs_torch(bmod, amod=None, S=37, Dm=24, Hq=4, Hkv=2, d=8):
+    """The block against torch: F.linear for each projection, bfloat16
+    conversion for the rounding, fp64 SDPA (GQA via repeated kv heads) for
+    the attention."""
+    x = _bf16_values((S, Dm), 63)
+    wq, wk, wv = _bf16_values((Hq * d, Dm), 64, 0.3), _bf16_values((Hkv * d, Dm), 65, 0.3), \
+        _bf16_values((Hkv * d, Dm), 66, 0.3)
+    wo = _bf16_values((Dm, Hq * d), 67, 0.3)
+    for causal in (True, False):
+        y, out, lse = bmod.attention_block_forward(x, wq, wk, wv, wo, Hq, Hkv, causal=causal)
+        rnd = lambda t: t.to(torch.float32).to(torch.bfloat16).to(torch.float64)  # noqa: E731
+        tx = torch.tensor(x)
+        q = rnd(F.linear(tx, torch.tensor(wq))).reshape(S, Hq, d).permute(1, 0, 2)
+        k = rnd(F.linear(tx, torch.tensor(wk))).reshape(S, Hkv, d).permute(1, 0, 2)
+        v = rnd(F.linear(tx, torch.tensor(wv))).reshape(S, Hkv, d).permute(1, 0, 2)
+        o = F.scaled_dot_product_attention(q.unsqueeze(0), k.repeat_interleave(Hq // Hkv, 0).unsqueeze(0),
+                                           v.repeat_interleave(Hq // Hkv, 0).unsqueeze(0), is_causal=causal)
+        o = o.squeeze(0).permute(1, 0, 2)
+        np.testing.assert_allclose(out, o.numpy(), rtol=1e-11, atol=1e-12)
+        ref_y = F.linear(rnd(o).reshape(S, Hq * d), torch.tensor(wo)).numpy()
+        np.testing.assert_allclose(y, ref_y, rtol=1e-10, atol=1e-11)
+
+
+def pin_block_identity_is_attention(bmod, amod, S=29, Hq=4, Hkv=2, d=8):
+    """With identity projections (Dm = Hq*d) the block is plain attention of
+    slices of x, and y its output rounded to bf16."""
+    Dm = Hq * d
+    x = _bf16_values((S, Dm), 68)
+    eye = np.eye(Dm)
+    wq, wk, wv, wo = eye, eye[:Hkv * d], eye[Hkv * d:2 * Hkv * d], eye
+    y, out, lse = bmod.attention_block_forward(x, wq, wk, wv, wo, Hq, Hkv)
+    o_ref, l_ref = amod.attention_forward(x.reshape(S, Hq, d), x[:, :Hkv * d].reshape(S, Hkv, d),
+                                          x[:, Hkv * d:2 * Hkv * d].reshape(S, Hkv, d))
+    np.testing.assert_array_equal(out, o_ref)
+    np.testing.assert_array_equal(lse, l_ref)
+    np.testing.assert_array_equal(y, bmod.round_bf16(o_ref).reshape(S, Dm))
+
+
+def pin_block_linear_in_wo_and_head_order(bmod, amod=None, S=23, Dm=16, Hq=4, Hkv=2, d=8):
+    """y is linear in Wo, and relabelling query heads inside a kv group (rows
+    of Wq and columns of Wo moved together) leaves y unchanged."""
+    x = _bf16_values((S, Dm), 69)
+    wq, wk, wv = _bf16_values((Hq * d, Dm), 70, 0.3), _bf16_values((Hkv * d, Dm), 71, 0.3), \
+        _bf16_values((Hkv * d, Dm), 72, 0.3)
+    wo1, wo2 = _bf16_values((Dm, Hq * d), 73, 0.3), _bf16_values((Dm, Hq * d), 74, 0.3)
+    y1 = bmod.attention_block_forward(x, wq, wk, wv, wo1, Hq, Hkv)[0]
+    y2 = bmod.attention_block_forward(x, wq, wk, wv, wo2, Hq, Hkv)[0]
+    y12 = bmod.attention_block_forward(x, wq, wk, wv, wo1 + wo2, Hq, Hkv)[0]
+    np.testing.assert_allclose(y12, y1 + y2, rtol=1e-12, atol=1e-12)
+    perm = [1, 0, 3, 2]  # swaps heads inside each group of G = 2
+    rows = np.concatenate([np.arange(h * d, (h + 1) * d) for h in perm])
+    yp = bmod.attention_block_forward(x, wq[rows], wk, wv, wo1[:, rows], Hq, Hkv)[0]
+    np.testing.assert_allclose(yp, y1, rtol=1e-12, atol=1e-12)
+
+
+def pin_block_rows(bmod, amod=None, S=41, Dm=16, Hq=4, Hkv=2, d=8):
+    """The sampled-row block function equals the full one at those rows."""
+    x = _bf16_values((S, Dm), 75)
+    wq, wk, wv = _bf16_values((Hq * d, Dm), 76, 0.3), _bf16_values((Hkv * d, Dm), 77, 0.3), \
+        _bf16_values((Hkv * d, Dm), 78, 0.3)
+    wo = _bf16_values((Dm, Hq * d), 79, 0.3)
+    rows = np.array([0, 1, 17, 40, 22, 7])
+    for causal in (True, False):
+        y, out, lse = bmod.attention_block_forward(x, wq, wk, wv, wo, Hq, Hkv, causal=causal)
+        yr, outr, lser = bmod.attention_block_rows(x, wq, wk, wv, wo, Hq, Hkv, rows, causal=causal)
+        np.testing.assert_allclose(yr, y[rows], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(outr, out[rows], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lser, lse[:, rows], rtol=1e-12, atol=1e-13)
+
+
+BLOCK_PINS = [pin_round_bf16, pin_block_vs_torch, pin_block_identity_is_attention,
+              pin_block_linear_in_wo_and_head_order, pin_block_rows]
+
+
+def failing_block_pins(bmod, amod):
+    bad = []
+    for pin in BLOCK_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(bmod, amod)
+        except Exception:  # noqa: BLE001
             bad.append(pin.__name__)
     return bad

@@ -225,3 +225,82 @@ def test_binding_checks_document_offsets(offsets, msg):
             L._require_docs(q, t)
     with pytest.raises(L.UpipeError, match="int32"):
         L._require_docs(q, t.long())
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,hcs", [(131072, 4, 1, 128, (1, 2, 4)), (5242880, 8, 1, 128, (1, 2, 4, 8)),
+                                            (1024, 4, 4, 64, (1, 4)), (1000, 8, 2, 128, (1, 2, 4, 8))])
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_workspace_bytes_is_the_larger_pool(S, Hq, Hkv, d, hcs, dtype):
+    """One workspace for the forward and the backward of a training step."""
+    prev = 0
+    for hc in hcs:
+        both = L.upipe_attn_workspace_bytes(S, Hq, Hkv, d, hc, dtype)
+        assert both == max(L.upipe_attn_fwd_workspace_bytes(S, Hq, Hkv, d, hc, dtype),
+                           L.upipe_attn_bwd_workspace_bytes(S, Hq, Hkv, d, hc, dtype))
+        assert both > prev
+        prev = both
+    assert L.lib().upipe_attn_workspace_bytes(S, Hq, Hkv, d, 3, dtype) == 0
+    assert "head_chunk" in L.upipe_last_error()
+
+
+def test_pick_head_chunk_takes_the_largest_pool_that_fits():
+    S, Hq, Hkv, d = 5242880, 8, 1, 128
+    sizes = {hc: L.upipe_attn_workspace_bytes(S, Hq, Hkv, d, hc, 0) for hc in (1, 2, 4, 8)}
+    for hc, n in sizes.items():
+        assert L.upipe_attn_pick_head_chunk(S, Hq, Hkv, d, 0, n) == hc
+        if hc > 1:
+            assert L.upipe_attn_pick_head_chunk(S, Hq, Hkv, d, 0, n - 1) == hc // 2
+    assert L.upipe_attn_pick_head_chunk(S, Hq, Hkv, d, 0, 1 << 50) == 8
+    # Hq = 6, Hkv = 2 (G = 3): the valid chunks are 1, 3, 6, never 2
+    sizes6 = {hc: L.upipe_attn_workspace_bytes(4096, 6, 2, 64, hc, 0) for hc in (1, 3, 6)}
+    assert L.upipe_attn_pick_head_chunk(4096, 6, 2, 64, 0, sizes6[3] + 100) == 3
+    assert L.upipe_attn_pick_head_chunk(4096, 6, 2, 64, 0, sizes6[6] - 1) == 3
+    with pytest.raises(L.UpipeError, match="even head_chunk 1"):
+        L.upipe_attn_pick_head_chunk(S, Hq, Hkv, d, 0, sizes[1] - 1)
+    with pytest.raises(L.UpipeError, match="head dim"):
+        L.upipe_attn_pick_head_chunk(S, Hq, Hkv, 96, 0, 1 << 50)
+
+
+def test_size_limits_at_the_boundary():
+    """S*d < 2^31 is the only length limit: copy kernels index tokens with 64
+    bits, so a total vector count at or above 2^32 (where a 32-bit grid-stride
+    index would wrap) is accepted. Host-only: sizes are computed, nothing runs."""
+    d = 128
+    assert L.upipe_attn_fwd_workspace_bytes((1 << 24) - 1, 1, 1, d, 1, 0) > 0  # S*d = 2^31 - 128
+    assert L.lib().upipe_attn_fwd_workspace_bytes(1 << 24, 1, 1, d, 1, 0) == 0  # S*d = 2^31
+    assert "2^31" in L.upipe_last_error()
+    # q with Hq = head_chunk = 64 at S = 4,193,000: 2^32 - 1.1e6 sixteen-byte vectors per pack
+    S, H = 4193000, 64
+    assert S * H * d * 2 // 16 > (1 << 32) - (1 << 21)
+    assert L.upipe_attn_fwd_workspace_bytes(S, H, 1, d, H, 0) > 0
+    # and past 2^32 vectors
+    assert S * 128 * d * 2 // 16 > (1 << 32)
+    assert L.upipe_attn_bwd_workspace_bytes(S, 128, 1, d, 128, 0) > 0
+
+
+def test_block_and_gemm_host_checks():
+    lib = L.lib()
+    S, Dm, Hq, Hkv, d = 4096, 512, 4, 1, 128
+    sizes = [L.upipe_attn_block_fwd_workspace_bytes(S, Dm, Hq, Hkv, d, hc) for hc in (1, 2, 4)]
+    assert sizes[0] < sizes[1] < sizes[2]
+    U = S * d * 2
+    assert sizes[0] >= 2 * U + 3 * U  # q, o; k, v, transposed v
+    assert lib.upipe_attn_block_fwd_workspace_bytes(S, 100, Hq, Hkv, d, 1) == 0
+    assert "multiple of 64" in L.upipe_last_error()
+    blk = lambda **kw: lib.upipe_attn_block_fwd(*(kw.get(n, FAKE) for n in ("x", "wq", "wk", "wv", "wo", "y")),  # noqa: E731
+                                                kw.get("out"), kw.get("lse", FAKE), S, kw.get("Dm", Dm), Hq, Hkv, d,
+                                                kw.get("hc", 1), 1, FAKE, kw.get("ws", 1 << 40), None)
+    assert blk(wo=None) == -1 and "wo is NULL" in L.upipe_last_error()
+    assert blk(Dm=96) == -2
+    assert blk(hc=3) == -1
+    assert blk(ws=16) == -3
+    assert blk(out=ctypes.c_void_p(0x10002)) == -1 and "out is not 16-byte aligned" in L.upipe_last_error()
+    gemm = lambda M=64, N=64, K=64, lda=64, a_km=1, c_dtype=1, acc=0, a=FAKE: lib.upipe_gemm_bf16(  # noqa: E731
+        a, lda, 0, 0, a_km, FAKE, K, 0, 0, 1, FAKE, N, 0, 0, c_dtype, acc, M, N, K, None)
+    assert gemm(K=100) == -2 and "multiple of 64" in L.upipe_last_error()
+    assert gemm(N=60) == -2
+    assert gemm(acc=1, c_dtype=0) == -1 and "fp32" in L.upipe_last_error()
+    assert gemm(lda=60) == -1
+    assert gemm(M=60, a_km=0, lda=64) == -1 and "multiple of 8" in L.upipe_last_error()
+    assert gemm(a=None) == -1 and "a is NULL" in L.upipe_last_error()
+    assert gemm(M=0) == -1

@@ -13,11 +13,10 @@ import pytest
 import torch
 
 import long_context_attention_upipe_amd as up
-from gpu_util import assert_close, bit_equal, f64, interleaved_parts, oracle_parallel, run
+from gpu_util import OracleJobs, assert_close, bit_equal, f64, grad_scale, interleaved_parts, run
 from long_context_attention_upipe_amd.workloads import (WORKLOADS, custom, doc_boundary_rows, doc_offsets,
                                                         make_inputs, sample_rows)
-from oracle.attention import (attention_backward, attention_forward, backward_cols_dkdv, backward_rows_dq,
-                              forward_rows)
+from oracle.attention import attention_backward, attention_forward, backward_cols_dkdv, rows_forward_dq
 
 pytestmark = pytest.mark.gpu
 
@@ -49,9 +48,10 @@ def _docs_case(w, offsets, hcs, causal=True, check_bwd=True):
         assert_close("out", f64(r["out"]), ro, w.dtype)
         assert_close("lse", f64(r["lse"]), rl, w.dtype)
         if check_bwd:
-            assert_close("dq", f64(r["dq"]), rdq, w.dtype)
-            assert_close("dk", f64(r["dk"]), rdk, w.dtype)
-            assert_close("dv", f64(r["dv"]), rdv, w.dtype)
+            gs = grad_scale(w)
+            assert_close("dq", f64(r["dq"]), rdq, w.dtype, grad_scale=gs, per_item=True)
+            assert_close("dk", f64(r["dk"]), rdk, w.dtype, grad_scale=gs, per_item=True)
+            assert_close("dv", f64(r["dv"]), rdv, w.dtype, grad_scale=gs, per_item=True)
         if first is None:
             first = r
         else:
@@ -147,44 +147,40 @@ def test_llama8b_share_1m_docs_sampled():
     print(f"\n  case {w.name} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} docs={len(offsets) - 1}", flush=True)
     q, k, v, do = make_inputs(w, device=dev)
     offs_t = torch.from_numpy(offsets).to(dev)
-    r = None
-    for hc in w.head_chunks:
-        print(f"   head_chunk={hc}", flush=True)
-        cur = run(q, k, v, do, hc, doc_offsets=offs_t)
-        if r is None:
-            r = cur
-        else:
-            for name in cur:
-                assert bit_equal(cur[name], r[name]), f"{name}: head_chunk {hc} differs"
-            del cur
-
     rows = np.union1d(sample_rows(w.S, 4096, seed=w.seed + 7), doc_boundary_rows(offsets, len(offsets), w.seed + 8))
     rows_t = torch.from_numpy(rows).to(dev)
     kc, vc = f64(k), f64(v)
     qr, dor = f64(q[rows_t]), f64(do[rows_t])
-    parts = interleaved_parts(len(rows), 64)
-    fwd = oracle_parallel(lambda p: forward_rows(qr[p], kc, vc, rows[p], doc_offsets=offsets), parts, "forward rows")
-    o_ref, l_ref = np.empty_like(qr), np.empty((w.Hq, len(rows)))
-    for p, (o, lse) in zip(parts, fwd):
-        o_ref[p], l_ref[:, p] = o, lse
-    assert_close("out", f64(r["out"][rows_t]), o_ref, w.dtype)
-    assert_close("lse", f64(r["lse"][:, rows_t]), l_ref, w.dtype)
-    dqs = oracle_parallel(lambda p: backward_rows_dq(qr[p], kc, vc, dor[p], rows[p], doc_offsets=offsets), parts,
-                          "dq rows")
-    dq_ref = np.empty_like(qr)
-    for p, dq in zip(parts, dqs):
-        dq_ref[p] = dq
-    assert_close("dq", f64(r["dq"][rows_t]), dq_ref, w.dtype)
-
-    print("   oracle: keys at document ends", flush=True)
-    ends = [int(offsets[m + 1]) for m in (0, 3, len(offsets) // 2, len(offsets) - 2)]
     q32, do32 = q.float().cpu().numpy(), do.float().cpu().numpy()
-    for end in ends:
-        keys = np.arange(end - 64, end, dtype=np.int64)
-        dk_ref, dv_ref = backward_cols_dkdv(q32, kc, vc, do32, keys, doc_offsets=offsets)
-        keys_t = torch.from_numpy(keys).to(dev)
-        assert_close("dk", f64(r["dk"][keys_t]), dk_ref, w.dtype)
-        assert_close("dv", f64(r["dv"][keys_t]), dv_ref, w.dtype)
+    ends = [int(offsets[m + 1]) for m in (0, 3, len(offsets) // 2, len(offsets) - 2)]
+    with OracleJobs() as jobs:
+        # host side, concurrent with the GPU runs below
+        parts = interleaved_parts(len(rows), 64)
+        rows_job = jobs.map(lambda p: rows_forward_dq(qr[p], kc, vc, dor[p], rows[p], doc_offsets=offsets), parts,
+                            "rows (O, LSE, dQ)")
+        keys_job = jobs.map(lambda end: backward_cols_dkdv(q32, kc, vc, do32, np.arange(end - 64, end, dtype=np.int64),
+                                                           doc_offsets=offsets), ends, "keys at document ends")
+        r = None
+        for hc in w.head_chunks:
+            print(f"   head_chunk={hc}", flush=True)
+            cur = run(q, k, v, do, hc, doc_offsets=offs_t)
+            if r is None:
+                r = cur
+            else:
+                for name in cur:
+                    assert bit_equal(cur[name], r[name]), f"{name}: head_chunk {hc} differs"
+                del cur
+        gs = grad_scale(w)
+        o_ref, l_ref, dq_ref = np.empty_like(qr), np.empty((w.Hq, len(rows))), np.empty_like(qr)
+        for p, (o, lse, dq) in zip(parts, jobs.gather(rows_job)):
+            o_ref[p], l_ref[:, p], dq_ref[p] = o, lse, dq
+        assert_close("out", f64(r["out"][rows_t]), o_ref, w.dtype, per_item=True)
+        assert_close("lse", f64(r["lse"][:, rows_t]), l_ref, w.dtype)
+        assert_close("dq", f64(r["dq"][rows_t]), dq_ref, w.dtype, grad_scale=gs, per_item=True)
+        for end, (dk_ref, dv_ref) in zip(ends, jobs.gather(keys_job)):
+            keys_t = torch.arange(end - 64, end, device=dev)
+            assert_close("dk", f64(r["dk"][keys_t]), dk_ref, w.dtype, grad_scale=gs, per_item=True)
+            assert_close("dv", f64(r["dv"][keys_t]), dv_ref, w.dtype, grad_scale=gs, per_item=True)
 
 
 @pytest.mark.slow
@@ -204,43 +200,43 @@ def test_llama8b_share_1m_docs_non_causal_sampled():
     print(f"\n  case {w.name} non-causal S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} docs={len(offsets) - 1}", flush=True)
     q, k, v, do = make_inputs(w, device=dev)
     offs_t = torch.from_numpy(offsets).to(dev)
-    r = None
-    for hc in w.head_chunks:
-        print(f"   head_chunk={hc}", flush=True)
-        cur = run(q, k, v, do, hc, causal=False, doc_offsets=offs_t)
-        if r is None:
-            r = cur
-        else:
-            for name in cur:
-                assert bit_equal(cur[name], r[name]), f"{name}: head_chunk {hc} differs"
-            del cur
-
     rows = np.union1d(sample_rows(w.S, 1024, seed=w.seed + 17), doc_boundary_rows(offsets, len(offsets), w.seed + 18))
     rows_t = torch.from_numpy(rows).to(dev)
     kc, vc = f64(k), f64(v)
     qr, dor = f64(q[rows_t]), f64(do[rows_t])
-    parts = interleaved_parts(len(rows), 64)
-    fwd = oracle_parallel(lambda p: forward_rows(qr[p], kc, vc, rows[p], causal=False, doc_offsets=offsets), parts,
-                          "forward rows")
-    o_ref, l_ref = np.empty_like(qr), np.empty((w.Hq, len(rows)))
-    for p, (o, lse) in zip(parts, fwd):
-        o_ref[p], l_ref[:, p] = o, lse
-    assert_close("out", f64(r["out"][rows_t]), o_ref, w.dtype)
-    assert_close("lse", f64(r["lse"][:, rows_t]), l_ref, w.dtype)
-    dqs = oracle_parallel(lambda p: backward_rows_dq(qr[p], kc, vc, dor[p], rows[p], causal=False,
-                                                     doc_offsets=offsets), parts, "dq rows")
-    dq_ref = np.empty_like(qr)
-    for p, dq in zip(parts, dqs):
-        dq_ref[p] = dq
-    assert_close("dq", f64(r["dq"][rows_t]), dq_ref, w.dtype)
-
-    print("   oracle: keys in the shortest documents", flush=True)
     lengths = np.diff(offsets)
-    for m in np.argsort(lengths, kind="stable")[:4]:
-        start, end = int(offsets[m]), int(offsets[m + 1])
+    short = [(int(offsets[m]), int(offsets[m + 1])) for m in np.argsort(lengths, kind="stable")[:4]]
+    q64, do64 = f64(q), f64(do)
+
+    def doc_keys(span):
+        start, end = span
         keys = np.arange(min(64, end - start), dtype=np.int64)
-        dk_ref, dv_ref = backward_cols_dkdv(f64(q[start:end]), kc[start:end], vc[start:end], f64(do[start:end]), keys,
-                                            causal=False)
-        keys_t = torch.from_numpy(keys + start).to(dev)
-        assert_close("dk", f64(r["dk"][keys_t]), dk_ref, w.dtype)
-        assert_close("dv", f64(r["dv"][keys_t]), dv_ref, w.dtype)
+        return backward_cols_dkdv(q64[start:end], kc[start:end], vc[start:end], do64[start:end], keys, causal=False)
+
+    with OracleJobs() as jobs:
+        # host side, concurrent with the GPU runs below
+        parts = interleaved_parts(len(rows), 64)
+        rows_job = jobs.map(lambda p: rows_forward_dq(qr[p], kc, vc, dor[p], rows[p], causal=False,
+                                                      doc_offsets=offsets), parts, "rows (O, LSE, dQ)")
+        keys_job = jobs.map(doc_keys, short, "keys in the shortest documents")
+        r = None
+        for hc in w.head_chunks:
+            print(f"   head_chunk={hc}", flush=True)
+            cur = run(q, k, v, do, hc, causal=False, doc_offsets=offs_t)
+            if r is None:
+                r = cur
+            else:
+                for name in cur:
+                    assert bit_equal(cur[name], r[name]), f"{name}: head_chunk {hc} differs"
+                del cur
+        gs = grad_scale(w)
+        o_ref, l_ref, dq_ref = np.empty_like(qr), np.empty((w.Hq, len(rows))), np.empty_like(qr)
+        for p, (o, lse, dq) in zip(parts, jobs.gather(rows_job)):
+            o_ref[p], l_ref[:, p], dq_ref[p] = o, lse, dq
+        assert_close("out", f64(r["out"][rows_t]), o_ref, w.dtype, per_item=True)
+        assert_close("lse", f64(r["lse"][:, rows_t]), l_ref, w.dtype)
+        assert_close("dq", f64(r["dq"][rows_t]), dq_ref, w.dtype, grad_scale=gs, per_item=True)
+        for (start, end), (dk_ref, dv_ref) in zip(short, jobs.gather(keys_job)):
+            keys_t = torch.arange(start, start + min(64, end - start), device=dev)
+            assert_close("dk", f64(r["dk"][keys_t]), dk_ref, w.dtype, grad_scale=gs, per_item=True)
+            assert_close("dv", f64(r["dv"][keys_t]), dv_ref, w.dtype, grad_scale=gs, per_item=True)

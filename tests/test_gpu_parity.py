@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import long_context_attention_upipe_amd as up
-from gpu_util import assert_close, bit_equal, f64, run
+from gpu_util import assert_close, bit_equal, f64, grad_scale, run
 from long_context_attention_upipe_amd.workloads import WORKLOADS, custom, make_inputs
 from oracle.attention import attention_backward, attention_forward
 
@@ -37,9 +37,10 @@ def _full_case(w, hcs, causal=True, check_bwd=True, rel_only=False):
         assert_close("out", f64(r["out"]), ro, w.dtype)
         assert_close("lse", f64(r["lse"]), rl, w.dtype)
         if check_bwd:
-            assert_close("dq", f64(r["dq"]), rdq, w.dtype, rel_only)
-            assert_close("dk", f64(r["dk"]), rdk, w.dtype, rel_only)
-            assert_close("dv", f64(r["dv"]), rdv, w.dtype, rel_only)
+            gs = grad_scale(w)
+            assert_close("dq", f64(r["dq"]), rdq, w.dtype, rel_only, grad_scale=gs, per_item=True)
+            assert_close("dk", f64(r["dk"]), rdk, w.dtype, rel_only, grad_scale=gs, per_item=True)
+            assert_close("dv", f64(r["dv"]), rdv, w.dtype, rel_only, grad_scale=gs, per_item=True)
         if first is None:
             first = r
         else:

@@ -38,6 +38,18 @@ MUTATIONS = {
     "docs_mask_replaces_causal": ("mask = outside if mask is None else (mask | outside)", "mask = outside"),
     "cols_docs_ignored": ("excluded = other_doc if excluded is None else (excluded | other_doc)", "pass"),
     "cols_docs_first_row": ("first = max(first, int(bounds[0][cols].min()))", "first = max(first, int(bounds[0][cols].max()))"),
+    "fused_rows_missing_D": ("            ds = p * (_rows_matmul(do_blk, v_g.T) - D[..., None])",
+                             "            ds = p * _rows_matmul(do_blk, v_g.T)"),
+    "fused_rows_dq_uses_v": ("            dq[np.ix_(sel, hs)] = tau * _rows_matmul(ds, k_g)",
+                             "            dq[np.ix_(sel, hs)] = tau * _rows_matmul(ds, v_g)"),
+    "fused_rows_dq_missing_tau": ("            dq[np.ix_(sel, hs)] = tau * _rows_matmul(ds, k_g)",
+                                  "            dq[np.ix_(sel, hs)] = _rows_matmul(ds, k_g)"),
+    "fused_rows_D_from_v": ("            D = (do_blk * o).sum(axis=-1)\n            ds = p * (_rows_matmul(do_blk, v_g.T)",
+                            "            D = (do_blk * v_g[:1]).sum(axis=-1)\n            ds = p * (_rows_matmul(do_blk, v_g.T)"),
+    "fused_rows_lse_transposed_heads": ("            lse[np.ix_(hs, sel)] = lse_blk.T\n            do_blk",
+                                        "            lse[np.ix_(hs, sel)] = lse_blk.T[::-1]\n            do_blk"),
+    "cols_row_stats_swapped": ("        o_need, lse_need = _f64(row_stats[0]), _f64(row_stats[1])",
+                               "        o_need, lse_need = _f64(row_stats[0]), _f64(row_stats[1])[::-1]"),
     "cols_docs_end_row": ("end = int(bounds[1][cols].max()) + 1", "end = int(bounds[1][cols].min()) + 1"),
 }
 
