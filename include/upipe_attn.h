@@ -152,6 +152,33 @@ int upipe_attn_bwd(const void* q, const void* k, const void* v,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Forward that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, results and errors as upipe_attn_fwd,
+ * bit for bit, without the workspace: the fixed buffer pool lives in a
+ * static device array of UPIPE_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU
+ * holds from the library's first call on it until the process ends. The
+ * forward's pool needs nothing cleared between calls (every byte a kernel
+ * reads is written earlier in the same call).
+ *   - Limit: upipe_attn_fwd_workspace_bytes(S, Hq, Hkv, d, head_chunk, dtype)
+ *     must not exceed UPIPE_NOALLOC_SCRATCH_BYTES (about 65,000 tokens at
+ *     Hkv = head_chunk = 1, d = 128, bf16); larger problems fail with
+ *     UPIPE_EWORKSPACE before anything is enqueued.
+ *   - The current device (hipSetDevice) must be the one that owns the tensors
+ *     and the stream: its copy of the array is used.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (other streams, other threads) race on it and must be
+ *     serialized by the caller. Calls in stream order are safe.
+ *   - No hipMalloc, hipFree or allocating library call is made; the array's
+ *     address is looked up once per device (hipGetSymbolAddress).
+ */
+#define UPIPE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int upipe_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                           void* out, void* out_lo, float* lse,
+                           int64_t S, int Hq, int Hkv, int d, int head_chunk,
+                           int causal, int dtype, void* stream);
+
+/*
  * Packed documents (MaxText long-context article: several samples packed into
  * one long sequence need no padding, and blocks that the mask excludes
  * entirely are skipped). The same forward and backward as above, where a

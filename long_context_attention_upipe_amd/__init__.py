@@ -6,6 +6,7 @@ helpers that let torch allocate the outputs and the fixed buffer pool.
 """
 
 from ._lib import (  # noqa: F401
+    NOALLOC_SCRATCH_BYTES,
     UPIPE_BF16,
     UPIPE_FP32,
     UpipeError,
@@ -17,6 +18,7 @@ from ._lib import (  # noqa: F401
     upipe_attn_bwd_workspace_bytes,
     upipe_attn_fwd,
     upipe_attn_fwd_docs,
+    upipe_attn_fwd_noalloc,
     upipe_attn_fwd_workspace_bytes,
     upipe_attn_pick_head_chunk,
     upipe_attn_plan,

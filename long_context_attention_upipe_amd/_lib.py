@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_block_fwd_workspace_bytes.restype = sz
     L.upipe_attn_block_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     L.upipe_attn_block_fwd.restype = i32
+    L.upipe_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
+    L.upipe_attn_fwd_noalloc.restype = i32
     # The packed-document entry points are bound when the loaded build has
     # them (UPIPE_ATTN_LIBRARY may name an older build); calling them on a
     # build without them raises AttributeError.
@@ -203,6 +205,26 @@ def upipe_attn_fwd(q, k, v, out, out_lo, lse, head_chunk, causal, workspace, str
         _check(lib().upipe_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(lse), S, Hq, Hkv, d,
                                     int(head_chunk), int(causal), dtype_code(q.dtype),
                                     _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+
+
+# Bytes of the static device array behind upipe_attn_fwd_noalloc (the
+# header's UPIPE_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def upipe_attn_fwd_noalloc(q, k, v, out, out_lo, lse, head_chunk, causal, stream=None) -> None:
+    """The forward without a workspace: the library's static per-GPU scratch
+    array holds the pool, and nothing is allocated. Calls that overlap in time
+    on one GPU race on that array; calls in stream order are safe."""
+    S, Hq, Hkv, d = _shape(q, k)
+    _require((q, k, v, out) + ((out_lo,) if out_lo is not None else ()), q.dtype)
+    _require((lse,), torch.float32)
+    _require_shapes(q, [("k", k, (S, Hkv, d)), ("v", v, (S, Hkv, d)), ("out", out, (S, Hq, d)),
+                        ("out_lo", out_lo, (S, Hq, d)), ("lse", lse, (Hq, S))])
+    with torch.cuda.device(q.device):
+        _check(lib().upipe_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(lse), S, Hq,
+                                            Hkv, d, int(head_chunk), int(causal), dtype_code(q.dtype),
+                                            _stream_handle(stream)))
 
 
 def upipe_attn_bwd(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, workspace, stream=None) -> None:

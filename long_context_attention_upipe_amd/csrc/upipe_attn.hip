@@ -590,7 +590,36 @@ int upipe_attn_pick_head_chunk(int64_t S, int Hq, int Hkv, int d, int dtype, siz
 
 }  // extern "C"
 
+// Scratch for upipe_attn_fwd_noalloc: the forward's fixed buffer pool in a
+// file-scope device array, so that entry point never allocates. Each GPU the
+// library runs on holds its own copy from the first call until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory:
+// its device address is looked up once per device (with that device current)
+// and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[UPIPE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr size_t kScratchBytes = UPIPE_NOALLOC_SCRATCH_BYTES;
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_addr;  // per device ordinal; null until looked up
+
+int scratch_address(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(UPIPE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((int)g_scratch_addr.size() <= dev) g_scratch_addr.resize(dev + 1, nullptr);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(UPIPE_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return UPIPE_OK;
+}
 
 // Packed-document arguments: a device array of n_docs + 1 offsets, or none.
 int validate_docs(const int32_t* doc_offsets, int n_docs, Problem* pr) {
@@ -697,6 +726,21 @@ int upipe_attn_bwd_docs(const void* q, const void* k, const void* v, const void*
   if (!doc_offsets && !n_docs) return fail(UPIPE_EINVAL, "doc_offsets is NULL");
   return bwd_entry(q, k, v, out, out_lo, dout, lse, dq, dk, dv, S, Hq, Hkv, d, head_chunk, causal, doc_offsets,
                    n_docs, dtype, workspace, workspace_bytes, stream);
+}
+
+int upipe_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, void* out_lo, float* lse,
+                           int64_t S, int Hq, int Hkv, int d, int head_chunk, int causal, int dtype,
+                           void* stream) {
+  Problem pr;
+  if (int rc = validate(S, Hq, Hkv, d, head_chunk, causal, dtype, &pr)) return rc;
+  const size_t need = fwd_pool(pr).total;
+  if (need > kScratchBytes)
+    return fail(UPIPE_EWORKSPACE, "forward pool needs %zu bytes, more than the %zu-byte static scratch array", need,
+                kScratchBytes);
+  void* ws = nullptr;
+  if (int rc = scratch_address(&ws)) return rc;
+  return fwd_entry(q, k, v, out, out_lo, lse, S, Hq, Hkv, d, head_chunk, causal, nullptr, 0, dtype, ws, kScratchBytes,
+                   stream);
 }
 
 int upipe_gemm_bf16(const void* a, int64_t lda, int64_t a_blk, int64_t a_blk_stride, int a_kmajor, const void* b,

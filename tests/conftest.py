@@ -35,5 +35,11 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # run cheap tests first, the full-size GPU cases last
-    items.sort(key=lambda it: 1 if it.get_closest_marker("slow") else 0)
+    # cheap tests first, then the full-size GPU cases, then the test_zz_*
+    # files, which must also pass after everything else has run
+    def rank(it):
+        if os.path.basename(str(it.fspath)).startswith("test_zz_"):
+            return 2
+        return 1 if it.get_closest_marker("slow") else 0
+
+    items.sort(key=rank)

@@ -278,6 +278,22 @@ def test_size_limits_at_the_boundary():
     assert L.upipe_attn_bwd_workspace_bytes(S, 128, 1, d, 128, 0) > 0
 
 
+def test_noalloc_forward_host_checks():
+    """upipe_attn_fwd_noalloc validates like the workspace forward and rejects
+    a pool larger than its static array before touching any device."""
+    lib = L.lib()
+    args = lambda S, hc=1, d=128: (FAKE, FAKE, FAKE, FAKE, None, FAKE, S, 4, 1, d, hc, 1, 0, None)  # noqa: E731
+    assert lib.upipe_attn_fwd_noalloc(*args(70000)) == -3
+    assert "static scratch" in L.upipe_last_error()
+    assert L.upipe_attn_fwd_workspace_bytes(70000, 4, 1, 128, 1, 0) > L.NOALLOC_SCRATCH_BYTES
+    assert lib.upipe_attn_fwd_noalloc(*args(1000, hc=3)) == -1
+    assert "must divide Hq" in L.upipe_last_error()
+    assert lib.upipe_attn_fwd_noalloc(*args(1000, d=96)) == -2
+    with open(HEADER) as f:
+        assert "#define UPIPE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in f.read()
+    assert L.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def test_block_and_gemm_host_checks():
     lib = L.lib()
     S, Dm, Hq, Hkv, d = 4096, 512, 4, 1, 128
