@@ -266,6 +266,87 @@ def run_one(w, head_chunk: int, steps: int, warmup: int, dev, residual: bool = T
     return res, tensors
 
 
+def block_sweep(w, dev, chunks, warmup=1):
+    """The attention block forward (q, k, v projections of each head chunk,
+    attention, its share of the output projection) at every head_chunk: time
+    for one call, peak HBM over the call (x, weights, y, lse and the pool; no
+    q, k, v or o of all heads exists) and the pool. Dm = Hq * d (the share's
+    heads as the whole model)."""
+    import torch
+
+    import long_context_attention_upipe_amd as up
+    from long_context_attention_upipe_amd.workloads import make_block_inputs
+
+    Dm = w.Hq * w.d
+    rows = []
+    for hc in chunks:
+        torch.cuda.synchronize(dev)
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+        x, wq, wk, wv, wo = make_block_inputs(w.S, Dm, w.Hq, w.Hkv, w.d, seed=w.seed + 50, device=dev)
+        y = torch.empty((w.S, Dm), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.Hq, w.S), dtype=torch.float32, device=dev)
+        ws = torch.empty(up.upipe_attn_block_fwd_workspace_bytes(w.S, Dm, w.Hq, w.Hkv, w.d, hc), dtype=torch.uint8,
+                         device=dev)
+        for _ in range(warmup):
+            up.upipe_attn_block_fwd(x, wq, wk, wv, wo, y, None, lse, w.Hq, w.Hkv, hc, True, ws)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        up.upipe_attn_block_fwd(x, wq, wk, wv, wo, y, None, lse, w.Hq, w.Hkv, hc, True, ws)
+        torch.cuda.synchronize(dev)
+        ms = (time.perf_counter() - t0) * 1e3
+        attn = 4 * w.d * w.Hq * pairs(w.S, True)
+        proj = 2 * w.S * Dm * (w.Hq + 2 * w.Hkv) * w.d + 2 * w.S * w.Hq * w.d * Dm
+        rows.append({"head_chunk": hc, "ms": round(ms, 2), "tflops": round((attn + proj) / (ms / 1e3) / 1e12, 2),
+                     "peak_hbm_gib": round((torch.cuda.max_memory_allocated(dev) - base) / GIB, 4),
+                     "pool_gib": round(ws.numel() / GIB, 4)})
+        print(f"[bench] block fwd head_chunk={hc}: {ms:.1f} ms, peak {rows[-1]['peak_hbm_gib']:.2f} GiB",
+              file=sys.stderr, flush=True)
+        del x, wq, wk, wv, wo, y, lse, ws
+    return {"Dm": Dm, "flops": "attention 4*d*Hq*S(S+1)/2 + projections 2*S*Dm*(Hq+2*Hkv)*d + 2*S*Hq*d*Dm",
+            "sweep": rows}
+
+
+def loss_leg(dev, S=131072, Dm=4096, V=128256, tile=4096):
+    """The sequence-tiled cross-entropy, forward and backward (loss, dh, dW),
+    on S tokens of a Llama-3-sized head (Dm 4096, vocabulary 128,256): one
+    timed call after one warm-up, its peak HBM and its bounded buffer against
+    the [S, V] fp32 logits it never forms."""
+    import torch
+
+    import long_context_attention_upipe_amd as up
+
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    h = torch.randn((S, Dm), generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn((V, Dm), generator=g, device=dev) / Dm ** 0.5).to(torch.bfloat16)
+    labels = torch.randint(0, V, (S,), generator=g, device=dev, dtype=torch.int32)
+    loss = torch.empty(S, device=dev)
+    dh = torch.empty_like(h)
+    dw = torch.empty((V, Dm), device=dev)
+    ws = torch.empty(up.upipe_ce_loss_workspace_bytes(S, Dm, V, tile, True), dtype=torch.uint8, device=dev)
+    up.upipe_ce_loss_tiled(h, w, labels, loss, dh, dw, tile, 1.0 / S, ws)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    up.upipe_ce_loss_tiled(h, w, labels, loss, dh, dw, tile, 1.0 / S, ws)
+    torch.cuda.synchronize(dev)
+    ms = (time.perf_counter() - t0) * 1e3
+    flops = 6 * S * Dm * V
+    res = {"S": S, "Dm": Dm, "V": V, "tile": tile, "ms": round(ms, 2),
+           "tflops": round(flops / (ms / 1e3) / 1e12, 2), "flops": "6*S*Dm*V (logits, dh, dW GEMMs)",
+           "peak_hbm_gib": round((torch.cuda.max_memory_allocated(dev) - base) / GIB, 3),
+           "buffer_gib": round(ws.numel() / GIB, 3), "full_logits_fp32_gib": round(S * V * 4 / GIB, 2)}
+    print(f"[bench] tiled loss: {ms:.1f} ms, {res['tflops']:.1f} TFLOP/s, peak {res['peak_hbm_gib']:.2f} GiB",
+          file=sys.stderr, flush=True)
+    del h, w, labels, loss, dh, dw, ws
+    return res
+
+
 def roofline(w, res, head_chunk):
     """Roofline entry for the attention kernel with the most time per step."""
     attn = {n: e for n, e in res["kernels"].items() if n in ALGO_FLOPS_PER_PAIR_D}
@@ -304,6 +385,9 @@ def main():
     ap.add_argument("--sweep-chunks", default=None, help="comma-separated head_chunk values for the sweep")
     ap.add_argument("--sweep-steps", type=int, default=2)
     ap.add_argument("--sweep-warmup", type=int, default=1)
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the attention-block forward sweep (projections around the chunk loop)")
+    ap.add_argument("--no-loss", action="store_true", help="skip the sequence-tiled cross-entropy leg")
     ap.add_argument("--no-residual-run", action="store_true",
                     help="skip the one-step run without out_lo (peak HBM when D comes from out alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -361,6 +445,11 @@ def main():
                   "steps": 1, "warmup": 0}
         print(f"[bench] without out_lo: peak {r['peak_hbm_gib']:.2f} GiB", file=sys.stderr, flush=True)
 
+    block = None
+    if not args.no_block and w.dtype == "bf16" and not w.doc_lengths:
+        block = block_sweep(w, dev, list(w.head_chunks))
+    loss_res = None if args.no_loss else loss_leg(dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         from long_context_attention_upipe_amd.workloads import make_inputs
@@ -408,6 +497,10 @@ def main():
     }
     if sweep:
         line["head_chunk_sweep"] = sweep
+    if block:
+        line["block_fwd"] = block
+    if loss_res:
+        line["tiled_loss"] = loss_res
     print(json.dumps(line), flush=True)
 
 

@@ -272,6 +272,31 @@ int upipe_attn_block_fwd(const void* x, const void* wq, const void* wk, const vo
                          int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Sequence-tiled cross-entropy over the vocabulary (talk summary, Chapters:
+ * the sequence-tiling chapter -- the loss is computed in pieces along the
+ * sequence so that the [S, V] logits never exist at once). Tiles of `tile`
+ * tokens go in ascending order through one bounded buffer of tile x V fp32
+ * logits (plus tile x V bf16 gradient rows when gradients are asked for):
+ *   z_i    = W h_i,  lse_i = ln sum_j exp(z_ij)
+ *   loss_i = lse_i - z_i[label_i]                     (0 if label_i < 0)
+ *   G_ij   = grad_scale * (exp(z_ij - lse_i) - [j == label_i])   (bf16)
+ *   dh_i   = sum_j G_ij W_j,   dw_j = sum_i G_ij h_i  (tile by tile, in order)
+ *   h      [S, Dm] bf16 (final hidden states), w [V, Dm] bf16 (torch Linear
+ *          layout), labels [S] int32 (negative: ignored)
+ *   loss   [S] fp32, natural log
+ *   dh     [S, Dm] bf16 or NULL; dw [V, Dm] fp32 or NULL (written, not
+ *          accumulated into); both NULL: forward only (no gradient buffer)
+ * Dm a multiple of 64, V a multiple of 8, tile a multiple of 64. Results are
+ * deterministic (fixed reduction and accumulation orders). Workspace:
+ * upipe_ce_loss_workspace_bytes(S, Dm, V, tile, with_grad), independent of S.
+ */
+size_t upipe_ce_loss_workspace_bytes(int64_t S, int Dm, int V, int tile, int with_grad);
+int upipe_ce_loss_tiled(const void* h, const void* w, const int32_t* labels, float* loss,
+                        void* dh, float* dw, int64_t S, int Dm, int V, int tile,
+                        float grad_scale, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * The head-chunk plan, for inspection (host only, no device work). Fills up to
  * max_chunks entries; entry c describes chunk c:
  *   q_head0[c]  first query head of the chunk (it covers head_chunk heads)

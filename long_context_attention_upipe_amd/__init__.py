@@ -23,6 +23,8 @@ from ._lib import (  # noqa: F401
     upipe_attn_pick_head_chunk,
     upipe_attn_plan,
     upipe_attn_workspace_bytes,
+    upipe_ce_loss_tiled,
+    upipe_ce_loss_workspace_bytes,
     upipe_gemm_bf16,
     upipe_last_error,
     upipe_profile_completed,

@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz,
                                  vp]
     L.upipe_attn_bwd.restype = i32
+    L.upipe_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
+    L.upipe_attn_fwd_noalloc.restype = i32
     L.upipe_gemm_bf16.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, i32, i32, i32,
                                   i32, i32, vp]
     L.upipe_gemm_bf16.restype = i32
@@ -62,8 +64,10 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_block_fwd_workspace_bytes.restype = sz
     L.upipe_attn_block_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     L.upipe_attn_block_fwd.restype = i32
-    L.upipe_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
-    L.upipe_attn_fwd_noalloc.restype = i32
+    L.upipe_ce_loss_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+    L.upipe_ce_loss_workspace_bytes.restype = sz
+    L.upipe_ce_loss_tiled.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, ctypes.c_float, vp, sz, vp]
+    L.upipe_ce_loss_tiled.restype = i32
     # The packed-document entry points are bound when the loaded build has
     # them (UPIPE_ATTN_LIBRARY may name an older build); calling them on a
     # build without them raises AttributeError.
@@ -400,3 +404,38 @@ def upipe_attn_block_fwd(x, wq, wk, wv, wo, y, out, lse, n_q_heads, n_kv_heads, 
         _check(lib().upipe_attn_block_fwd(_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(y), _ptr(out),
                                           _ptr(lse), S, Dm, Hq, Hkv, d, int(head_chunk), int(causal),
                                           _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+
+
+def upipe_ce_loss_workspace_bytes(S, Dm, V, tile, with_grad=True) -> int:
+    n = lib().upipe_ce_loss_workspace_bytes(S, Dm, V, tile, int(bool(with_grad)))
+    if n == 0:
+        raise UpipeError(-1, upipe_last_error())
+    return n
+
+
+def upipe_ce_loss_tiled(h, w, labels, loss, dh, dw, tile, grad_scale, workspace, stream=None) -> None:
+    """Cross-entropy of h [S, Dm] (bf16) against labels [S] (int32, < 0
+    ignored) through the vocabulary projection w [V, Dm] (bf16, torch Linear
+    layout), one tile of tokens at a time: loss [S] fp32; when given, dh
+    [S, Dm] bf16 and dw [V, Dm] fp32 (written, not accumulated into) are the
+    gradients of sum(grad_scale * loss)."""
+    if h.dim() != 2 or w.dim() != 2:
+        raise UpipeError(-1, "h and w must be 2-D")
+    S, Dm = h.shape
+    V = w.shape[0]
+    _require((h, w) + ((dh,) if dh is not None else ()), torch.bfloat16)
+    _require((loss,) + ((dw,) if dw is not None else ()), torch.float32)
+    _require((labels,), torch.int32)
+    _require((workspace,), torch.uint8)
+    for name, t, shape in (("w", w, (V, Dm)), ("labels", labels, (S,)), ("loss", loss, (S,)), ("dh", dh, (S, Dm)),
+                           ("dw", dw, (V, Dm)), ("workspace", workspace, (workspace.numel(),))):
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(shape):
+            raise UpipeError(-1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.device != h.device:
+            raise UpipeError(-1, f"{name} is on {t.device}, h on {h.device}")
+    with torch.cuda.device(h.device):
+        _check(lib().upipe_ce_loss_tiled(_ptr(h), _ptr(w), _ptr(labels), _ptr(loss), _ptr(dh), _ptr(dw), S, Dm, V,
+                                         int(tile), float(grad_scale), _ptr(workspace), workspace.numel(),
+                                         _stream_handle(stream)))

@@ -36,6 +36,8 @@ struct GemmOperand {
   int64_t blk;         // block length of the contiguous index (a multiple of 8)
   int64_t blk_stride;  // distance between blocks, elements
   int kmajor;          // 1: K contiguous; 0: M (or N) contiguous
+  int kvalid;          // M/N-contiguous operand: rows k >= kvalid (> 0) are read as row kvalid - 1,
+                       // for a K padded to the 64-deep step (the other operand holds zeros there)
 };
 
 // C[m, n] at p + (n / blk) * blk_stride + m * ldc + (n % blk).
@@ -83,8 +85,8 @@ __device__ __forceinline__ void gemm_load_tile(bf16* tile, const GemmOperand& op
       const int i = i0 * 4 + wave, slot = i * 64 + lane;
       const int r = slot / CPR, pos = slot % CPR, c = pos ^ swz<D, MODE>(r);
       const int mn = min(mn0 + c * 8, MN - 8);
-      __builtin_amdgcn_global_load_lds((const void*)gemm_elem(op, mn, (int64_t)k0 + r), (lds_void*)(tile + i * 512),
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)gemm_elem(op, mn, min(k0 + r, op.kvalid - 1)),
+                                       (lds_void*)(tile + i * 512), 16, 0, 0);
     }
   }
 }

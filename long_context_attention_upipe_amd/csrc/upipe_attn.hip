@@ -28,6 +28,7 @@
 #include "attn_fwd.hpp"
 #include "copy_kernels.hpp"
 #include "gemm_bf16.hpp"
+#include "loss_kernels.hpp"
 
 namespace upipe {
 namespace {
@@ -166,9 +167,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 // ---------------------------------------------------------------------------
 // Optional per-kernel timing with HIP events on the launch stream.
 // ---------------------------------------------------------------------------
-enum KernelId { K_PACK = 0, K_UNPACK, K_FWD, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_GEMM, K_COUNT };
+enum KernelId { K_PACK = 0, K_UNPACK, K_FWD, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_GEMM, K_CE_ROWS, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"pack_heads", "unpack_heads", "attn_fwd", "bwd_pre", "attn_bwd_dkdv",
-                                           "attn_bwd_dq", "gemm_bf16"};
+                                           "attn_bwd_dq", "gemm_bf16", "ce_rows"};
 struct Profiler {
   std::atomic<bool> on{false};
   struct Rec {
@@ -404,13 +405,15 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
 // ---------------------------------------------------------------------------
 constexpr int64_t kUnblocked = (int64_t)1 << 62;  // a contiguous index that never wraps
 
-GemmOperand operand(const void* p, int64_t ld, int kmajor, int64_t blk = kUnblocked, int64_t blk_stride = 0) {
+GemmOperand operand(const void* p, int64_t ld, int kmajor, int64_t blk = kUnblocked, int64_t blk_stride = 0,
+                    int kvalid = 1 << 30) {
   GemmOperand o;
   o.p = reinterpret_cast<const bf16*>(p);
   o.ld = ld;
   o.blk = blk;
   o.blk_stride = blk_stride;
   o.kmajor = kmajor;
+  o.kvalid = kvalid;
   return o;
 }
 
@@ -539,6 +542,72 @@ int run_block_fwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
       timed(K_GEMM, st, [&] { (void)gemm(oa, wob, yout, S, Dm, D, h > 0, st); });
     }
     if (int rc = check_launch("attention block chunk")) return rc;
+  }
+  return UPIPE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Sequence-tiled cross-entropy (loss_kernels.hpp). Pool: one tile's fp32
+// logits [tile][Vp] and its bf16 gradient rows [tile][Vp], Vp = V rounded up
+// to 64 (zero columns past V), reused by every tile.
+// ---------------------------------------------------------------------------
+int64_t vocab_pad(int V) { return ((int64_t)V + 63) / 64 * 64; }
+struct LossPool {
+  size_t logits, g, total;
+};
+LossPool loss_pool(int tile, int V, bool grad) {
+  LossPool p;
+  size_t off = 0;
+  p.logits = off; off += align_up((size_t)tile * vocab_pad(V) * 4);
+  p.g = off; off += grad ? align_up((size_t)tile * vocab_pad(V) * 2) : 0;
+  p.total = off;
+  return p;
+}
+
+int validate_loss(int64_t S, int Dm, int V, int tile) {
+  if (S < 1 || S >= (1ll << 31)) return fail(UPIPE_EINVAL, "S must be in [1, 2^31) (got %lld)", (long long)S);
+  if (Dm < 64 || Dm % 64) return fail(UPIPE_EUNSUPPORTED, "model dim Dm (%d) must be a positive multiple of 64", Dm);
+  if (V < 8 || V % 8) return fail(UPIPE_EUNSUPPORTED, "vocabulary size V (%d) must be a positive multiple of 8", V);
+  if (tile < 64 || tile % 64) return fail(UPIPE_EINVAL, "tile (%d) must be a positive multiple of 64", tile);
+  if ((uint64_t)tile * vocab_pad(V) * 4 >= (1ull << 40)) return fail(UPIPE_EUNSUPPORTED, "tile x V too large");
+  return UPIPE_OK;
+}
+
+int run_ce_loss(const bf16* h, const bf16* w, const int32_t* labels, float* loss, bf16* dh, float* dw, int64_t S64,
+                int Dm, int V, int tile, float scale, char* ws, hipStream_t st) {
+  const bool grad = dh || dw;
+  const LossPool pool = loss_pool(tile, V, grad);
+  const int S = (int)S64;
+  const int64_t Vp = vocab_pad(V);
+  float* logits = reinterpret_cast<float*>(ws + pool.logits);
+  bf16* G = grad ? reinterpret_cast<bf16*>(ws + pool.g) : nullptr;
+  const GemmOperand wk = operand(w, Dm, 1);  // W [V][Dm]: logits = h W^T
+  // W as [K = V][N = Dm] for dh = G W, K padded to Vp: rows past V are read as
+  // row V - 1, against G's zero columns
+  const GemmOperand wn = operand(w, Dm, 0, kUnblocked, 0, V);
+  const GemmOperand gk = operand(G, Vp, 1);  // G [tile][Vp], K = vocab contiguous
+  const GemmOperand gm = operand(G, Vp, 0);  // G^T: M = vocab contiguous, K = token (zero rows past T)
+  for (int t0 = 0; t0 < S; t0 += tile) {
+    const int T = std::min(tile, S - t0);
+    const GemmOperand hk = operand(h + (int64_t)t0 * Dm, Dm, 1);  // the tile's rows of h, K = Dm
+    // as [K = token][N = Dm] for dW = G^T h, K padded to the tile: tokens past
+    // T are read as token T - 1, against G's zero rows
+    const GemmOperand hn = operand(h + (int64_t)t0 * Dm, Dm, 0, kUnblocked, 0, T);
+    GemmOut<float> lo = {logits, Vp, kUnblocked, 0};
+    timed(K_GEMM, st, [&] { (void)gemm(hk, wk, lo, T, V, Dm, 0, st); });
+    timed(K_CE_ROWS, st, [&] {
+      hipLaunchKernelGGL(ce_rows_kernel, dim3(grad ? tile : T), dim3(256), 0, st, logits, (int)Vp, labels + t0,
+                         loss + t0, G, (int)Vp, T, V, scale);
+    });
+    if (dh) {
+      GemmOut<bf16> o = {dh + (int64_t)t0 * Dm, Dm, kUnblocked, 0};
+      timed(K_GEMM, st, [&] { (void)gemm(gk, wn, o, T, Dm, (int)Vp, 0, st); });
+    }
+    if (dw) {
+      GemmOut<float> o = {dw, Dm, kUnblocked, 0};
+      timed(K_GEMM, st, [&] { (void)gemm(gm, hn, o, V, Dm, tile, t0 > 0, st); });
+    }
+    if (int rc = check_launch("cross-entropy tile")) return rc;
   }
   return UPIPE_OK;
 }
@@ -802,6 +871,33 @@ int upipe_attn_block_fwd(const void* x, const void* wq, const void* wk, const vo
   char* ws = reinterpret_cast<char*>(workspace);
   if (d == 128) return run_block_fwd<128>(pr, Dm, x, wq, wk, wv, wo, y, out, lse, ws, st);
   return run_block_fwd<64>(pr, Dm, x, wq, wk, wv, wo, y, out, lse, ws, st);
+}
+
+size_t upipe_ce_loss_workspace_bytes(int64_t S, int Dm, int V, int tile, int with_grad) {
+  if (validate_loss(S, Dm, V, tile) != UPIPE_OK) return 0;
+  g_error.clear();
+  return loss_pool(tile, V, with_grad != 0).total;
+}
+
+int upipe_ce_loss_tiled(const void* h, const void* w, const int32_t* labels, float* loss, void* dh, float* dw,
+                        int64_t S, int Dm, int V, int tile, float grad_scale, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (int rc = validate_loss(S, Dm, V, tile)) return rc;
+  const void* ptrs[] = {h, w, labels, loss, workspace};
+  const char* names[] = {"h", "w", "labels", "loss", "workspace"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(UPIPE_EINVAL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  if ((dh && !aligned16(dh)) || (dw && !aligned16(dw))) return fail(UPIPE_EINVAL, "dh or dw is not 16-byte aligned");
+  const size_t need = loss_pool(tile, V, dh || dw).total;
+  if (workspace_bytes < need)
+    return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  g_error.clear();
+  (void)hipGetLastError();
+  return run_ce_loss(reinterpret_cast<const bf16*>(h), reinterpret_cast<const bf16*>(w), labels, loss,
+                     reinterpret_cast<bf16*>(dh), dw, S, Dm, V, tile, grad_scale, reinterpret_cast<char*>(workspace),
+                     reinterpret_cast<hipStream_t>(stream));
 }
 
 int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks, int32_t* q_head0, int32_t* kv_head0,

@@ -485,3 +485,51 @@ def failing_block_pins(bmod, amod):
         except Exception:  # noqa: BLE001
             bad.append(pin.__name__)
     return bad
+
+
+
+# --- the sequence-tiled cross-entropy -----------------------------------------
+
+def pin_ce_vs_torch(lmod, S=53, Dm=16, V=40):
+    """loss against torch's cross_entropy (fp64, no reduction, ignore_index
+    -100), dh and dW against its autograd of sum(scale * loss)."""
+    h, w = _rand((S, Dm), 81), _rand((V, Dm), 82) * 0.5
+    labels = np.random.default_rng(83).integers(0, V, size=S)
+    labels[[3, 17, 40]] = -100
+    scale = 0.37
+    loss, dh, dw = lmod.cross_entropy(h, w, labels, scale=scale, block=7)
+    th, tw = torch.tensor(h, requires_grad=True), torch.tensor(w, requires_grad=True)
+    ref = F.cross_entropy(F.linear(th, tw), torch.tensor(labels), reduction="none", ignore_index=-100)
+    np.testing.assert_allclose(loss, ref.detach().numpy(), rtol=1e-12, atol=1e-12)
+    (scale * ref).sum().backward()
+    np.testing.assert_allclose(dh, th.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dw, tw.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def pin_ce_closed_forms(lmod, S=9, Dm=4, V=16):
+    """W = 0: every logit is 0, so loss = ln V and G = scale (1/V - onehot);
+    dW rows then sum (over the vocabulary) to zero, as softmax rows sum to 1."""
+    h = _rand((S, Dm), 84)
+    labels = np.arange(S) % V
+    loss, dh, dw = lmod.cross_entropy(h, np.zeros((V, Dm)), labels, scale=2.0)
+    np.testing.assert_allclose(loss, np.log(V), rtol=1e-14)
+    np.testing.assert_allclose(dh, 0.0, atol=1e-15)
+    onehot = np.eye(V)[labels]
+    np.testing.assert_allclose(dw, 2.0 * (1.0 / V - onehot).T @ h, rtol=1e-12, atol=1e-13)
+    w = _rand((V, Dm), 85)
+    _, _, dw = lmod.cross_entropy(h, w, labels)
+    np.testing.assert_allclose(dw.sum(axis=0), 0.0, atol=1e-12)
+
+
+CE_PINS = [pin_ce_vs_torch, pin_ce_closed_forms]
+
+
+def failing_ce_pins(lmod):
+    bad = []
+    for pin in CE_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(lmod)
+        except Exception:  # noqa: BLE001
+            bad.append(pin.__name__)
+    return bad

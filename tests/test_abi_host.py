@@ -320,3 +320,23 @@ def test_block_and_gemm_host_checks():
     assert gemm(M=60, a_km=0, lda=64) == -1 and "multiple of 8" in L.upipe_last_error()
     assert gemm(a=None) == -1 and "a is NULL" in L.upipe_last_error()
     assert gemm(M=0) == -1
+
+
+def test_tiled_loss_host_checks():
+    lib = L.lib()
+    # the buffer is one tile's logits (+ its gradient rows), whatever S is
+    a = L.upipe_ce_loss_workspace_bytes(1 << 20, 4096, 128256, 2048, True)
+    b = L.upipe_ce_loss_workspace_bytes(5 << 20, 4096, 128256, 2048, True)
+    assert a == b
+    Vp = (128256 + 63) // 64 * 64
+    assert a >= 2048 * Vp * (4 + 2)
+    assert L.upipe_ce_loss_workspace_bytes(1 << 20, 4096, 128256, 2048, False) < a
+    call = lambda **kw: lib.upipe_ce_loss_tiled(  # noqa: E731
+        kw.get("h", FAKE), FAKE, FAKE, FAKE, None, None, kw.get("S", 1000), kw.get("Dm", 128), kw.get("V", 1000),
+        kw.get("tile", 128), 1.0, FAKE, kw.get("ws", 1 << 40), None)
+    assert call(V=1001) == -2 and "multiple of 8" in L.upipe_last_error()
+    assert call(tile=100) == -1 and "tile" in L.upipe_last_error()
+    assert call(Dm=100) == -2
+    assert call(h=None) == -1 and "h is NULL" in L.upipe_last_error()
+    assert call(ws=16) == -3
+    assert call(S=0) == -1
