@@ -21,12 +21,22 @@
 
 namespace upipe {
 
+// Tile sizes of the bf16 kernels. The host sizes their grids from these same
+// constants (one workgroup per kFwdRows query rows, per kDqRows rows, per
+// kDkvKeys keys of each head), so a kernel and its launch cannot disagree.
+struct Bf16Tiles {
+  static constexpr int kFwdRows = 128, kFwdKeys = 64;  // forward: rows per workgroup, keys per tile
+  static constexpr int kDqRows = 128, kDqKeys = 64;    // dQ: rows per workgroup, keys per tile
+  static constexpr int kDkvKeys = 128, kDkvRows = 32;  // dK/dV: keys per workgroup, rows per step
+};
+
 // ---------------------------------------------------------------------------
 // Forward: 4 waves x 32 query rows, 64-key tiles.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p) {
-  constexpr int BQ = 128, BK = 64, NKS = D / 16, NDB = D / 32;
+  constexpr int BQ = Bf16Tiles::kFwdRows, BK = Bf16Tiles::kFwdKeys, NKS = D / 16, NDB = D / 32;
+  static_assert(BQ == 4 * 32 && BK == 64, "4 waves x 32 rows; two 32-key blocks per tile");
   // K tiles [BK keys][D]; V tiles transposed, [D][BK positions] (pack_vt_kernel
   // blocks, one contiguous block per tile), so both operands are read as
   // 16-byte row fragments. Both layouts
@@ -186,7 +196,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16> p) {
-  constexpr int BQ = 128, BK = 64, NKS = D / 16, NDB = D / 32;
+  constexpr int BQ = Bf16Tiles::kDqRows, BK = Bf16Tiles::kDqKeys, NKS = D / 16, NDB = D / 32;
+  static_assert(BQ == 4 * 32 && BK == 64, "4 waves x 32 rows; two 32-key blocks per tile");
   __shared__ __attribute__((aligned(1024))) bf16 sK[2][BK * D];
   __shared__ __attribute__((aligned(1024))) bf16 sV[2][BK * D];
 
@@ -322,7 +333,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf16> p) {
-  constexpr int BKV = 128, BQ = 32, NKS = D / 16, NDB = D / 32;
+  constexpr int BKV = Bf16Tiles::kDkvKeys, BQ = Bf16Tiles::kDkvRows, NKS = D / 16, NDB = D / 32;
+  static_assert(BKV == 4 * 32 && BQ == 32, "4 waves x 32 keys; 32-row steps");
   // These tiles use the layout with both read kinds conflict-free (kSwzAll):
   // this kernel issues the most LDS reads per MFMA.
   __shared__ __attribute__((aligned(1024))) bf16 sQ[2][BQ * D];

@@ -164,6 +164,16 @@ BwdPool bwd_pool(const Problem& pr) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Grid extents of the attention kernels: the bf16 kernels' tiles for bf16,
+// the generic kernels' shapes for fp32.
+template <typename T, int D>
+struct Tiles {
+  static constexpr bool kBf16 = std::is_same<T, bf16>::value;
+  static constexpr int fwd_rows = kBf16 ? Bf16Tiles::kFwdRows : FwdShape<T, D>::BQ;
+  static constexpr int dq_rows = kBf16 ? Bf16Tiles::kDqRows : DqShape<T, D>::BQ;
+  static constexpr int dkv_keys = kBf16 ? Bf16Tiles::kDkvKeys : DkvShape<T, D>::BKV;
+};
+
 // ---------------------------------------------------------------------------
 // Optional per-kernel timing with HIP events on the launch stream.
 // ---------------------------------------------------------------------------
@@ -253,7 +263,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
   T* Oc = reinterpret_cast<T*>(ws + pool.o);
   T* Kc = reinterpret_cast<T*>(ws + pool.k);
   T* Vc = reinterpret_cast<T*>(ws + pool.v);
-  const int n_qtiles = (S + FwdShape<T, D>::BQ - 1) / FwdShape<T, D>::BQ;
+  const int n_qtiles = (S + Tiles<T, D>::fwd_rows - 1) / Tiles<T, D>::fwd_rows;
   const float scale = 1.0f / std::sqrt((float)D);
   for (const Chunk& c : plan(pr)) {
     if (c.load_kv) {
@@ -323,8 +333,8 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
   float* L2c = reinterpret_cast<float*>(ws + pool.lse2);
   float* dKa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dk_acc) : nullptr;
   float* dVa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dv_acc) : nullptr;
-  const int n_qtiles = (S + DqShape<T, D>::BQ - 1) / DqShape<T, D>::BQ;
-  const int n_ktiles = (S + DkvShape<T, D>::BKV - 1) / DkvShape<T, D>::BKV;
+  const int n_qtiles = (S + Tiles<T, D>::dq_rows - 1) / Tiles<T, D>::dq_rows;
+  const int n_ktiles = (S + Tiles<T, D>::dkv_keys - 1) / Tiles<T, D>::dkv_keys;
   const float scale = 1.0f / std::sqrt((float)D);
   constexpr int kRowsPerPreBlock = 256 / (D * (int)sizeof(T) / 16);
   for (const Chunk& c : plan(pr)) {
@@ -484,7 +494,7 @@ int run_block_fwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
   bf16* Kc = reinterpret_cast<bf16*>(ws + pool.k);
   bf16* Vtmp = reinterpret_cast<bf16*>(ws + pool.vtmp);
   bf16* Vt = reinterpret_cast<bf16*>(ws + pool.vt);
-  const int n_qtiles = (S + 127) / 128;
+  const int n_qtiles = (S + Bf16Tiles::kFwdRows - 1) / Bf16Tiles::kFwdRows;
   const float scale = 1.0f / std::sqrt((float)D);
   const int64_t SD = (int64_t)S * D;
   const GemmOperand xa = operand(x, Dm, 1);  // [S][Dm], K = Dm contiguous
