@@ -226,13 +226,15 @@ int upipe_attn_bwd_docs(const void* q, const void* k, const void* v,
  * (A stored [K][M], B stored [K][N]) -- and
  *   element (c, o) at ptr + (c / blk) * blk_stride + o * ld + (c % blk),
  * c the contiguous index, o the other one; blk <= 0 means one block (a plain
- * row-major matrix), blk > 0 lets the contiguous index run in blocks (a
- * head-major [heads][S][d] buffer read as one [S][heads * d] matrix). C is
+ * row-major matrix), blk > 0 (a power of two >= 8) lets the contiguous index
+ * run in blocks (a head-major [heads][S][d] buffer read as one
+ * [S][heads * d] matrix). C is
  *   C[m, n] at c + (n / c_blk) * c_blk_stride + m * ldc + (n % c_blk),
  * bf16 (c_dtype = UPIPE_BF16, rounded to nearest even) or fp32.
  * Requirements: K a multiple of 64; N a multiple of 8; an M- (N-)contiguous
- * operand needs M (N) a multiple of 8; every ld, block length and block
- * stride a multiple of 8 elements; pointers 16-byte aligned; M, N >= 1.
+ * operand needs M (N) a multiple of 8; every ld and block stride a multiple
+ * of 8 elements, every block length a power of two >= 8; pointers 16-byte
+ * aligned; M, N >= 1.
  * Device pointers, owned by the caller; the extents the layouts reach must lie
  * inside the caller's buffers (not checkable here: plain pointers). Errors as
  * for the attention calls; the work is enqueued on `stream`.

@@ -17,7 +17,9 @@
 // values a lane supplies for a 16-deep MFMA step are k = 4h..4h+3 and
 // 8+4h..8+4h+3 (h = lane half); mn-major tiles give that order with the
 // transposed LDS read, k-major tiles with two 8-byte reads. So any pair of
-// layouts feeds v_mfma_f32_32x32x16_bf16 without a transposing copy.
+// layouts feeds v_mfma_f32_32x32x16_bf16 without a transposing copy. When
+// both operands are k-major they use the plain order instead, one 16-byte
+// LDS read per fragment.
 #pragma once
 
 #include <type_traits>
@@ -29,23 +31,24 @@ namespace upipe {
 
 // Element (c, o) of an operand, c its contiguous index (K for k-major, M or N
 // for mn-major) and o the other one, lives at
-//   p + (c / blk) * blk_stride + o * ld + (c % blk).
+//   p + (c >> blk_shift) * blk_stride + o * ld + (c & (2^blk_shift - 1)),
+// i.e. the contiguous index runs in blocks of 2^blk_shift elements (>= 8).
 struct GemmOperand {
   const bf16* p;
   int64_t ld;          // stride of the other index, elements
-  int64_t blk;         // block length of the contiguous index (a multiple of 8)
+  int blk_shift;       // log2 of the block length of the contiguous index
   int64_t blk_stride;  // distance between blocks, elements
   int kmajor;          // 1: K contiguous; 0: M (or N) contiguous
   int kvalid;          // M/N-contiguous operand: rows k >= kvalid (> 0) are read as row kvalid - 1,
                        // for a K padded to the 64-deep step (the other operand holds zeros there)
 };
 
-// C[m, n] at p + (n / blk) * blk_stride + m * ldc + (n % blk).
+// C[m, n] at p + (n >> blk_shift) * blk_stride + m * ldc + (n & (2^blk_shift - 1)).
 template <typename CT>
 struct GemmOut {
   CT* p;
   int64_t ldc;
-  int64_t blk;  // a multiple of 8
+  int blk_shift;  // log2 of the block length of n (>= 3)
   int64_t blk_stride;
 };
 
@@ -58,17 +61,17 @@ struct GemmParams {
 };
 
 __device__ __forceinline__ const bf16* gemm_elem(const GemmOperand& op, int64_t c, int64_t o) {
-  return op.p + (c / op.blk) * op.blk_stride + o * op.ld + (c % op.blk);
+  return op.p + (c >> op.blk_shift) * op.blk_stride + o * op.ld + (c & ((int64_t(1) << op.blk_shift) - 1));
 }
 
 // Copy one operand's slice of a K tile into LDS. k-major: [128 mn][64 k]
 // tile (row = mn); mn-major: [64 k][128 mn] tile (row = k). Indices past the
 // matrix (ragged M or N) are clamped to its last row or chunk: those lanes'
 // results are never stored.
-template <int MODE>
+template <int KMAJOR, int MODE>
 __device__ __forceinline__ void gemm_load_tile(bf16* tile, const GemmOperand& op, int mn0, int MN, int k0, int wave,
                                                int lane) {
-  if (op.kmajor) {
+  if constexpr (KMAJOR) {
     constexpr int D = 64, CPR = D / 8, INSTR = 128 * CPR / 64;
 #pragma unroll
     for (int i0 = 0; i0 < INSTR / 4; ++i0) {
@@ -92,26 +95,34 @@ __device__ __forceinline__ void gemm_load_tile(bf16* tile, const GemmOperand& op
 }
 
 // Operand fragment for MFMA step ks (k = 16 ks .. 16 ks + 15 of the tile) and
-// the 32-row block mb of the operand's 128 M (or N) rows, in the k order of a
-// P fragment (see the file comment).
-template <int MODE>
-__device__ __forceinline__ bf16x8 gemm_frag(const bf16* tile, int kmajor, int ks, int mb, int lane) {
-  if (kmajor) {
+// the 32-row block mb of the operand's 128 M (or N) rows. NATURAL (both
+// operands k-major): lane half h supplies k = 8h .. 8h + 7, one 16-byte read.
+// Otherwise the k order of a P fragment (see the file comment): a transposed
+// read for an mn-major tile, two 8-byte reads for a k-major one.
+template <int KMAJOR, int NATURAL, int MODE>
+__device__ __forceinline__ bf16x8 gemm_frag(const bf16* tile, int ks, int mb, int lane) {
+  if constexpr (KMAJOR) {
     const int row = mb * 32 + (lane & 31), half = lane >> 5;
+    if constexpr (NATURAL) return tile_row_frag<64, MODE>(tile, row, 2 * ks + half);
     const bf16* p0 = tile + tile_off<64, MODE>(row, 2 * ks) + 4 * half;
     const bf16* p1 = tile + tile_off<64, MODE>(row, 2 * ks + 1) + 4 * half;
     const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p0);
     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p1);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    return tile_tr_frag<128, MODE>(tile, 16 * ks, mb * 32, lane);
   }
-  return tile_tr_frag<128, MODE>(tile, 16 * ks, mb * 32, lane);
 }
 
 // 4 waves, 128 x 128 tile of C per workgroup, each wave 64 x 64 (2 x 2 MFMA
-// tiles of 32 x 32), K in steps of 64, LDS double-buffered (64 KiB).
-template <typename CT>
+// tiles of 32 x 32), K in steps of 64, LDS double-buffered (64 KiB). Each K
+// step first reads all of its fragments from LDS into registers and only then
+// issues the copies of the next K tile into the other buffer, so those copies
+// fly while the MFMAs run (LDS reads issued after a copy would wait for it).
+template <typename CT, int AK, int BK>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams<CT> p) {
   constexpr int MODE = kSwzAll;
+  constexpr int NATURAL = AK && BK;
   __shared__ __attribute__((aligned(1024))) bf16 sA[2][128 * 64];
   __shared__ __attribute__((aligned(1024))) bf16 sB[2][128 * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -125,30 +136,31 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams<CT> p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
 
-  gemm_load_tile<MODE>(sA[0], p.a, m0, p.M, 0, wave, lane);
-  gemm_load_tile<MODE>(sB[0], p.b, n0, p.N, 0, wave, lane);
+  gemm_load_tile<AK, MODE>(sA[0], p.a, m0, p.M, 0, wave, lane);
+  gemm_load_tile<BK, MODE>(sB[0], p.b, n0, p.N, 0, wave, lane);
   wait_vm();
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      gemm_load_tile<MODE>(sA[cur ^ 1], p.a, m0, p.M, (kt + 1) * 64, wave, lane);
-      gemm_load_tile<MODE>(sB[cur ^ 1], p.b, n0, p.N, (kt + 1) * 64, wave, lane);
-    }
+    bf16x8 af[4][2], bfr[4][2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 af[2], bfr[2];
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        af[i] = gemm_frag<MODE>(sA[cur], p.a.kmajor, ks, wm + i, lane);
-        bfr[i] = gemm_frag<MODE>(sB[cur], p.b.kmajor, ks, wn + i, lane);
+        af[ks][i] = gemm_frag<AK, NATURAL, MODE>(sA[cur], ks, wm + i, lane);
+        bfr[ks][i] = gemm_frag<BK, NATURAL, MODE>(sB[cur], ks, wn + i, lane);
       }
+    if (kt + 1 < nk) {
+      gemm_load_tile<AK, MODE>(sA[cur ^ 1], p.a, m0, p.M, (kt + 1) * 64, wave, lane);
+      gemm_load_tile<BK, MODE>(sB[cur ^ 1], p.b, n0, p.N, (kt + 1) * 64, wave, lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
       // C^T tiles: lane = m (column of C^T), registers = n
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma32(acc[i][j], bfr[j], af[i]);
-    }
+        for (int j = 0; j < 2; ++j) mma32(acc[i][j], bfr[ks][j], af[ks][i]);
     wait_vm();
     __syncthreads();
   }
@@ -164,7 +176,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams<CT> p) {
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + (wn + j) * 32 + 8 * g + 4 * half;  // registers 4g .. 4g+3: n .. n+3
         if (n >= p.N) continue;
-        CT* dst = p.c.p + (n / p.c.blk) * p.c.blk_stride + (int64_t)m * p.c.ldc + (n % p.c.blk);
+        const int sh = min(p.c.blk_shift, 31);  // n < 2^31: a shift of 31 leaves block 0
+        CT* dst = p.c.p + (int64_t)((unsigned)n >> sh) * p.c.blk_stride + (int64_t)m * p.c.ldc +
+                  ((unsigned)n & ((1u << sh) - 1u));
         floatx4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];

@@ -415,16 +415,29 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
 // ---------------------------------------------------------------------------
 constexpr int64_t kUnblocked = (int64_t)1 << 62;  // a contiguous index that never wraps
 
+// log2 of a block length that is a power of two >= 8, else -1.
+int block_shift(int64_t blk) {
+  if (blk < 8 || (blk & (blk - 1))) return -1;
+  int sh = 0;
+  while ((int64_t(1) << sh) < blk) ++sh;
+  return sh;
+}
+
 GemmOperand operand(const void* p, int64_t ld, int kmajor, int64_t blk = kUnblocked, int64_t blk_stride = 0,
                     int kvalid = 1 << 30) {
   GemmOperand o;
   o.p = reinterpret_cast<const bf16*>(p);
   o.ld = ld;
-  o.blk = blk;
+  o.blk_shift = block_shift(blk);
   o.blk_stride = blk_stride;
   o.kmajor = kmajor;
   o.kvalid = kvalid;
   return o;
+}
+
+template <typename CT>
+GemmOut<CT> gemm_out(CT* p, int64_t ldc, int64_t blk = kUnblocked, int64_t blk_stride = 0) {
+  return GemmOut<CT>{p, ldc, block_shift(blk), blk_stride};
 }
 
 int check_operand(const char* name, const GemmOperand& o, int MN, int K) {
@@ -432,8 +445,9 @@ int check_operand(const char* name, const GemmOperand& o, int MN, int K) {
   if ((uintptr_t)o.p % 16) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", name);
   if (o.ld < 1 || o.ld % 8) return fail(UPIPE_EINVAL, "%s: leading dimension %lld is not a positive multiple of 8",
                                         name, (long long)o.ld);
-  if (o.blk < 8 || o.blk % 8 || (o.blk < kUnblocked && (o.blk_stride < 0 || o.blk_stride % 8)))
-    return fail(UPIPE_EINVAL, "%s: block length must be a multiple of 8 and the block stride of 8", name);
+  if (o.blk_shift < 3 || (o.blk_shift < 62 && (o.blk_stride < 0 || o.blk_stride % 8)))
+    return fail(UPIPE_EINVAL, "%s: block length must be a power of two >= 8 and the block stride a multiple of 8",
+                name);
   if (!o.kmajor && MN % 8) return fail(UPIPE_EINVAL, "%s: an M/N-contiguous operand needs M or N a multiple of 8", name);
   (void)K;
   return UPIPE_OK;
@@ -450,8 +464,15 @@ int gemm(const GemmOperand& a, const GemmOperand& b, const GemmOut<CT>& c, int M
   p.N = N;
   p.K = K;
   p.accumulate = accumulate;
-  hipLaunchKernelGGL((gemm_bf16_kernel<CT>), dim3((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128)),
-                     dim3(256), 0, st, p);
+  const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128));
+  if (a.kmajor && b.kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<CT, 1, 1>), grid, dim3(256), 0, st, p);
+  else if (a.kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<CT, 1, 0>), grid, dim3(256), 0, st, p);
+  else if (b.kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<CT, 0, 1>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<CT, 0, 0>), grid, dim3(256), 0, st, p);
   return check_launch("gemm");
 }
 
@@ -503,8 +524,8 @@ int run_block_fwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
       // k of the chunk's kv heads, head-major [nkv][S][D]; v token-major [S][nkv*D]
       const GemmOperand wkb = operand(reinterpret_cast<const bf16*>(wk) + (int64_t)c.kv_head0 * D * Dm, Dm, 1);
       const GemmOperand wvb = operand(reinterpret_cast<const bf16*>(wv) + (int64_t)c.kv_head0 * D * Dm, Dm, 1);
-      GemmOut<bf16> kout = {Kc, D, D, SD};
-      GemmOut<bf16> vout = {Vtmp, (int64_t)c.n_kv * D, kUnblocked, 0};
+      GemmOut<bf16> kout = gemm_out(Kc, D, D, SD);
+      GemmOut<bf16> vout = gemm_out(Vtmp, (int64_t)c.n_kv * D);
       timed(K_GEMM, st, [&] { (void)gemm(xa, wkb, kout, S, c.n_kv * D, Dm, 0, st); });
       timed(K_GEMM, st, [&] { (void)gemm(xa, wvb, vout, S, c.n_kv * D, Dm, 0, st); });
       timed(K_PACK, st, [&] {
@@ -513,7 +534,7 @@ int run_block_fwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
       });
     }
     const GemmOperand wqb = operand(reinterpret_cast<const bf16*>(wq) + (int64_t)c.q_head0 * D * Dm, Dm, 1);
-    GemmOut<bf16> qout = {Qc, D, D, SD};
+    GemmOut<bf16> qout = gemm_out(Qc, D, D, SD);
     timed(K_GEMM, st, [&] { (void)gemm(xa, wqb, qout, S, pr.hc * D, Dm, 0, st); });
     FwdParams<bf16> fp;
     fp.Sp = (int)vt_len(pr);
@@ -548,7 +569,7 @@ int run_block_fwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
       const int h = c.q_head0 + hl;
       const GemmOperand oa = operand(Oc + (int64_t)hl * SD, D, 1);
       const GemmOperand wob = operand(reinterpret_cast<const bf16*>(wo) + (int64_t)h * D, (int64_t)pr.Hq * D, 1);
-      GemmOut<float> yout = {y, Dm, kUnblocked, 0};
+      GemmOut<float> yout = gemm_out(y, Dm);
       timed(K_GEMM, st, [&] { (void)gemm(oa, wob, yout, S, Dm, D, h > 0, st); });
     }
     if (int rc = check_launch("attention block chunk")) return rc;
@@ -603,18 +624,18 @@ int run_ce_loss(const bf16* h, const bf16* w, const int32_t* labels, float* loss
     // as [K = token][N = Dm] for dW = G^T h, K padded to the tile: tokens past
     // T are read as token T - 1, against G's zero rows
     const GemmOperand hn = operand(h + (int64_t)t0 * Dm, Dm, 0, kUnblocked, 0, T);
-    GemmOut<float> lo = {logits, Vp, kUnblocked, 0};
+    GemmOut<float> lo = gemm_out(logits, Vp);
     timed(K_GEMM, st, [&] { (void)gemm(hk, wk, lo, T, V, Dm, 0, st); });
     timed(K_CE_ROWS, st, [&] {
       hipLaunchKernelGGL(ce_rows_kernel, dim3(grad ? tile : T), dim3(256), 0, st, logits, (int)Vp, labels + t0,
                          loss + t0, G, (int)Vp, T, V, scale);
     });
     if (dh) {
-      GemmOut<bf16> o = {dh + (int64_t)t0 * Dm, Dm, kUnblocked, 0};
+      GemmOut<bf16> o = gemm_out(dh + (int64_t)t0 * Dm, (int64_t)Dm);
       timed(K_GEMM, st, [&] { (void)gemm(gk, wn, o, T, Dm, (int)Vp, 0, st); });
     }
     if (dw) {
-      GemmOut<float> o = {dw, Dm, kUnblocked, 0};
+      GemmOut<float> o = gemm_out(dw, (int64_t)Dm);
       timed(K_GEMM, st, [&] { (void)gemm(gm, hn, o, V, Dm, tile, t0 > 0, st); });
     }
     if (int rc = check_launch("cross-entropy tile")) return rc;
@@ -838,17 +859,17 @@ int upipe_gemm_bf16(const void* a, int64_t lda, int64_t a_blk, int64_t a_blk_str
   if (!c) return fail(UPIPE_EINVAL, "c is NULL");
   if ((uintptr_t)c % 16) return fail(UPIPE_EINVAL, "c is not 16-byte aligned");
   const int64_t cb = c_blk > 0 ? c_blk : kUnblocked;
-  if (ldc < 1 || ldc % 8 || cb % 8 || (cb < kUnblocked && c_blk_stride % 8))
-    return fail(UPIPE_EINVAL, "c: ldc, block length and block stride must be multiples of 8");
+  if (ldc < 1 || ldc % 8 || block_shift(cb) < 3 || (cb < kUnblocked && c_blk_stride % 8))
+    return fail(UPIPE_EINVAL, "c: ldc and block stride must be multiples of 8, the block length a power of two >= 8");
   g_error.clear();
   (void)hipGetLastError();
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int rc;
   timed(K_GEMM, st, [&] {
     if (c_dtype == UPIPE_FP32)
-      rc = gemm(ao, bo, GemmOut<float>{reinterpret_cast<float*>(c), ldc, cb, c_blk_stride}, M, N, K, accumulate, st);
+      rc = gemm(ao, bo, gemm_out(reinterpret_cast<float*>(c), ldc, cb, c_blk_stride), M, N, K, accumulate, st);
     else
-      rc = gemm(ao, bo, GemmOut<bf16>{reinterpret_cast<bf16*>(c), ldc, cb, c_blk_stride}, M, N, K, 0, st);
+      rc = gemm(ao, bo, gemm_out(reinterpret_cast<bf16*>(c), ldc, cb, c_blk_stride), M, N, K, 0, st);
   });
   return rc;
 }
