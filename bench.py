@@ -347,6 +347,53 @@ def loss_leg(dev, S=131072, Dm=4096, V=128256, tile=4096):
     return res
 
 
+def mlp_leg(dev, S=131072, Dm=4096, F=14336, tile=4096):
+    """The sequence-tiled SwiGLU MLP, forward and backward, on S tokens of a
+    Llama-3-8B-sized MLP (Dm 4096, F 14336): one timed fwd+bwd after one
+    warm-up, its peak HBM and its bounded buffer against the [S, F] gate, up
+    and activation tensors it never forms."""
+    import torch
+
+    import long_context_attention_upipe_amd as up
+
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(78)
+    x = torch.randn((S, Dm), generator=g, device=dev).to(torch.bfloat16)
+    wg = (torch.randn((F, Dm), generator=g, device=dev) / Dm ** 0.5).to(torch.bfloat16)
+    wu = (torch.randn((F, Dm), generator=g, device=dev) / Dm ** 0.5).to(torch.bfloat16)
+    wd = (torch.randn((Dm, F), generator=g, device=dev) / F ** 0.5).to(torch.bfloat16)
+    dy = (torch.randn((S, Dm), generator=g, device=dev) / S).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    dx = torch.empty((S, Dm), device=dev)
+    dwg, dwu = torch.empty((F, Dm), device=dev), torch.empty((F, Dm), device=dev)
+    dwd = torch.empty((Dm, F), device=dev)
+    ws = torch.empty(up.upipe_mlp_workspace_bytes(S, Dm, F, tile, True), dtype=torch.uint8, device=dev)
+
+    def step():
+        up.upipe_mlp_tiled_fwd(x, wg, wu, wd, y, tile, ws)
+        up.upipe_mlp_tiled_bwd(x, wg, wu, wd, dy, dx, dwg, dwu, dwd, tile, ws)
+
+    step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize(dev)
+    ms = (time.perf_counter() - t0) * 1e3
+    flops = 11 * 2 * S * Dm * F  # fwd 3 GEMMs; bwd 2 recomputed, da, dx (2), dWg, dWu, dWd
+    res = {"S": S, "Dm": Dm, "F": F, "tile": tile, "ms": round(ms, 2),
+           "tflops": round(flops / (ms / 1e3) / 1e12, 2), "flops": "11 GEMMs of 2*S*Dm*F (fwd 3, bwd 8 incl. the recomputed gate/up)",
+           "peak_hbm_gib": round((torch.cuda.max_memory_allocated(dev) - base) / GIB, 3),
+           "buffer_gib": round(ws.numel() / GIB, 3), "untiled_intermediates_bf16_gib": round(3 * S * F * 2 / GIB, 2)}
+    print(f"[bench] tiled MLP: {ms:.1f} ms, {res['tflops']:.1f} TFLOP/s, peak {res['peak_hbm_gib']:.2f} GiB",
+          file=sys.stderr, flush=True)
+    del x, wg, wu, wd, dy, y, dx, dwg, dwu, dwd, ws
+    return res
+
+
 def roofline(w, res, head_chunk):
     """Roofline entry for the attention kernel with the most time per step."""
     attn = {n: e for n, e in res["kernels"].items() if n in ALGO_FLOPS_PER_PAIR_D}
@@ -388,6 +435,7 @@ def main():
     ap.add_argument("--no-block", action="store_true",
                     help="skip the attention-block forward sweep (projections around the chunk loop)")
     ap.add_argument("--no-loss", action="store_true", help="skip the sequence-tiled cross-entropy leg")
+    ap.add_argument("--no-mlp", action="store_true", help="skip the sequence-tiled MLP leg")
     ap.add_argument("--no-residual-run", action="store_true",
                     help="skip the one-step run without out_lo (peak HBM when D comes from out alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -449,6 +497,7 @@ def main():
     if not args.no_block and w.dtype == "bf16" and not w.doc_lengths:
         block = block_sweep(w, dev, list(w.head_chunks))
     loss_res = None if args.no_loss else loss_leg(dev)
+    mlp_res = None if args.no_mlp else mlp_leg(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -501,6 +550,8 @@ def main():
         line["block_fwd"] = block
     if loss_res:
         line["tiled_loss"] = loss_res
+    if mlp_res:
+        line["tiled_mlp"] = mlp_res
     print(json.dumps(line), flush=True)
 
 

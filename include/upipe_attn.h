@@ -299,6 +299,31 @@ int upipe_ce_loss_tiled(const void* h, const void* w, const int32_t* labels, flo
                         void* stream);
 
 /*
+ * Sequence-tiled SwiGLU MLP (talk summary, Chapters: the sequence-tiling
+ * chapter -- the MLP is computed in pieces along the sequence so that its
+ * [S, F] intermediates never exist at once). Tiles of `tile` tokens, in
+ * ascending order, through one bounded buffer of [tile, F] gate, up and
+ * activation rows:
+ *   g = x Wg^T, u = x Wu^T  (bf16),  a = silu(g) * u  (bf16),  y = a Wd^T
+ *   x, y [S, Dm] bf16; wg, wu [F, Dm], wd [Dm, F] bf16 (torch Linear layout)
+ * The backward recomputes each tile's g, u, a from x, then
+ *   da = dy Wd,  du = da * silu(g),  dg = da * u * silu'(g)   (dg, du bf16)
+ *   dx = dg Wg + du Wu   (fp32, written per tile)
+ *   dwg = sum over tiles dg^T x,  dwu = ... du^T x,  dwd = ... dy^T a   (fp32,
+ *   tiles in order: deterministic; written, not accumulated into)
+ * Dm, F and tile multiples of 64. Workspace: upipe_mlp_workspace_bytes
+ * (independent of S).
+ */
+size_t upipe_mlp_workspace_bytes(int64_t S, int Dm, int F, int tile, int with_grad);
+int upipe_mlp_tiled_fwd(const void* x, const void* wg, const void* wu, const void* wd, void* y,
+                        int64_t S, int Dm, int F, int tile,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int upipe_mlp_tiled_bwd(const void* x, const void* wg, const void* wu, const void* wd,
+                        const void* dy, float* dx, float* dwg, float* dwu, float* dwd,
+                        int64_t S, int Dm, int F, int tile,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The head-chunk plan, for inspection (host only, no device work). Fills up to
  * max_chunks entries; entry c describes chunk c:
  *   q_head0[c]  first query head of the chunk (it covers head_chunk heads)

@@ -26,6 +26,9 @@ from ._lib import (  # noqa: F401
     upipe_ce_loss_tiled,
     upipe_ce_loss_workspace_bytes,
     upipe_gemm_bf16,
+    upipe_mlp_tiled_bwd,
+    upipe_mlp_tiled_fwd,
+    upipe_mlp_workspace_bytes,
     upipe_last_error,
     upipe_profile_completed,
     upipe_profile_enable,

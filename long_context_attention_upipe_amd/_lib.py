@@ -68,6 +68,12 @@ def lib() -> ctypes.CDLL:
     L.upipe_ce_loss_workspace_bytes.restype = sz
     L.upipe_ce_loss_tiled.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, ctypes.c_float, vp, sz, vp]
     L.upipe_ce_loss_tiled.restype = i32
+    L.upipe_mlp_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+    L.upipe_mlp_workspace_bytes.restype = sz
+    L.upipe_mlp_tiled_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, sz, vp]
+    L.upipe_mlp_tiled_fwd.restype = i32
+    L.upipe_mlp_tiled_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, sz, vp]
+    L.upipe_mlp_tiled_bwd.restype = i32
     # The packed-document entry points are bound when the loaded build has
     # them (UPIPE_ATTN_LIBRARY may name an older build); calling them on a
     # build without them raises AttributeError.
@@ -439,3 +445,50 @@ def upipe_ce_loss_tiled(h, w, labels, loss, dh, dw, tile, grad_scale, workspace,
         _check(lib().upipe_ce_loss_tiled(_ptr(h), _ptr(w), _ptr(labels), _ptr(loss), _ptr(dh), _ptr(dw), S, Dm, V,
                                          int(tile), float(grad_scale), _ptr(workspace), workspace.numel(),
                                          _stream_handle(stream)))
+
+
+def upipe_mlp_workspace_bytes(S, Dm, F, tile, with_grad=True) -> int:
+    n = lib().upipe_mlp_workspace_bytes(S, Dm, F, tile, int(bool(with_grad)))
+    if n == 0:
+        raise UpipeError(-1, upipe_last_error())
+    return n
+
+
+def _mlp_shapes(x, wg, wu, wd, named):
+    if x.dim() != 2 or wg.dim() != 2:
+        raise UpipeError(-1, "x and the weights must be 2-D")
+    S, Dm = x.shape
+    F = wg.shape[0]
+    for name, t, shape in [("wg", wg, (F, Dm)), ("wu", wu, (F, Dm)), ("wd", wd, (Dm, F))] + named(S, Dm, F):
+        if tuple(t.shape) != tuple(shape):
+            raise UpipeError(-1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.device != x.device:
+            raise UpipeError(-1, f"{name} is on {t.device}, x on {x.device}")
+    return S, Dm, F
+
+
+def upipe_mlp_tiled_fwd(x, wg, wu, wd, y, tile, workspace, stream=None) -> None:
+    """y = (silu(x Wg^T) * (x Wu^T)) Wd^T, one tile of tokens at a time.
+    x [S, Dm], wg, wu [F, Dm], wd [Dm, F] (torch Linear layout), y [S, Dm]:
+    all bf16."""
+    _require((x, wg, wu, wd, y), torch.bfloat16)
+    _require((workspace,), torch.uint8)
+    S, Dm, F = _mlp_shapes(x, wg, wu, wd, lambda S, Dm, F: [("y", y, (S, Dm))])
+    with torch.cuda.device(x.device):
+        _check(lib().upipe_mlp_tiled_fwd(_ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(y), S, Dm, F, int(tile),
+                                         _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+
+
+def upipe_mlp_tiled_bwd(x, wg, wu, wd, dy, dx, dwg, dwu, dwd, tile, workspace, stream=None) -> None:
+    """Gradients of the tiled SwiGLU MLP given dy [S, Dm] (bf16): dx [S, Dm]
+    and dwg, dwu [F, Dm], dwd [Dm, F], all fp32, written (not accumulated
+    into). Each tile's activations are recomputed from x."""
+    _require((x, wg, wu, wd, dy), torch.bfloat16)
+    _require((dx, dwg, dwu, dwd), torch.float32)
+    _require((workspace,), torch.uint8)
+    S, Dm, F = _mlp_shapes(x, wg, wu, wd, lambda S, Dm, F: [
+        ("dy", dy, (S, Dm)), ("dx", dx, (S, Dm)), ("dwg", dwg, (F, Dm)), ("dwu", dwu, (F, Dm)), ("dwd", dwd, (Dm, F))])
+    with torch.cuda.device(x.device):
+        _check(lib().upipe_mlp_tiled_bwd(_ptr(x), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(dy), _ptr(dx), _ptr(dwg),
+                                         _ptr(dwu), _ptr(dwd), S, Dm, F, int(tile), _ptr(workspace),
+                                         workspace.numel(), _stream_handle(stream)))

@@ -29,6 +29,7 @@
 #include "copy_kernels.hpp"
 #include "gemm_bf16.hpp"
 #include "loss_kernels.hpp"
+#include "mlp_kernels.hpp"
 
 namespace upipe {
 namespace {
@@ -177,9 +178,9 @@ struct Tiles {
 // ---------------------------------------------------------------------------
 // Optional per-kernel timing with HIP events on the launch stream.
 // ---------------------------------------------------------------------------
-enum KernelId { K_PACK = 0, K_UNPACK, K_FWD, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_GEMM, K_CE_ROWS, K_COUNT };
+enum KernelId { K_PACK = 0, K_UNPACK, K_FWD, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_GEMM, K_CE_ROWS, K_SWIGLU, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"pack_heads", "unpack_heads", "attn_fwd", "bwd_pre", "attn_bwd_dkdv",
-                                           "attn_bwd_dq", "gemm_bf16", "ce_rows"};
+                                           "attn_bwd_dq", "gemm_bf16", "ce_rows", "swiglu"};
 struct Profiler {
   std::atomic<bool> on{false};
   struct Rec {
@@ -643,6 +644,112 @@ int run_ce_loss(const bf16* h, const bf16* w, const int32_t* labels, float* loss
   return UPIPE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Sequence-tiled SwiGLU MLP (mlp_kernels.hpp). Pool: one tile's gate and up
+// rows g, u and activation a [tile][F] bf16, and for the backward the fp32
+// da [tile][F]; reused by every tile, independent of S.
+// ---------------------------------------------------------------------------
+struct MlpPool {
+  size_t g, u, a, da, total;
+};
+MlpPool mlp_pool(int F, int tile, bool grad) {
+  const size_t B = (size_t)tile * F * 2;
+  MlpPool p;
+  size_t off = 0;
+  p.g = off; off += align_up(B);
+  p.u = off; off += align_up(B);
+  p.a = off; off += align_up(B);
+  p.da = off; off += grad ? align_up(2 * B) : 0;
+  p.total = off;
+  return p;
+}
+
+int validate_mlp(int64_t S, int Dm, int F, int tile) {
+  if (S < 1 || S >= (1ll << 31)) return fail(UPIPE_EINVAL, "S must be in [1, 2^31) (got %lld)", (long long)S);
+  if (Dm < 64 || Dm % 64) return fail(UPIPE_EUNSUPPORTED, "model dim Dm (%d) must be a positive multiple of 64", Dm);
+  if (F < 64 || F % 64) return fail(UPIPE_EUNSUPPORTED, "hidden dim F (%d) must be a positive multiple of 64", F);
+  if (tile < 64 || tile % 64) return fail(UPIPE_EINVAL, "tile (%d) must be a positive multiple of 64", tile);
+  if ((uint64_t)tile * F * 10 >= (1ull << 40)) return fail(UPIPE_EUNSUPPORTED, "tile x F too large");
+  return UPIPE_OK;
+}
+
+// g, u and a of one tile of T tokens starting at token t0 (rows T..tile-1 of a
+// zeroed when zero_tail); returns the launch status.
+int mlp_tile_forward(const bf16* x, const bf16* wg, const bf16* wu, int t0, int T, int Dm, int F, int tile,
+                     const MlpPool& pool, char* ws, bool zero_tail, hipStream_t st) {
+  bf16* g = reinterpret_cast<bf16*>(ws + pool.g);
+  bf16* u = reinterpret_cast<bf16*>(ws + pool.u);
+  bf16* a = reinterpret_cast<bf16*>(ws + pool.a);
+  const GemmOperand xk = operand(x + (int64_t)t0 * Dm, Dm, 1);  // the tile's rows of x, K = Dm
+  timed(K_GEMM, st, [&] { (void)gemm(xk, operand(wg, Dm, 1), gemm_out(g, (int64_t)F), T, F, Dm, 0, st); });
+  timed(K_GEMM, st, [&] { (void)gemm(xk, operand(wu, Dm, 1), gemm_out(u, (int64_t)F), T, F, Dm, 0, st); });
+  timed(K_SWIGLU, st, [&] {
+    hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(zero_tail ? tile : T), dim3(256), 0, st, g, u, a, T, F);
+  });
+  return check_launch("swiglu forward");
+}
+
+int run_mlp_fwd(const bf16* x, const bf16* wg, const bf16* wu, const bf16* wd, bf16* y, int S, int Dm, int F,
+                int tile, char* ws, hipStream_t st) {
+  const MlpPool pool = mlp_pool(F, tile, false);
+  const bf16* a = reinterpret_cast<const bf16*>(ws + pool.a);
+  for (int t0 = 0; t0 < S; t0 += tile) {
+    const int T = std::min(tile, S - t0);
+    if (int rc = mlp_tile_forward(x, wg, wu, t0, T, Dm, F, tile, pool, ws, false, st)) return rc;
+    // y = a Wd^T: Wd [Dm][F] is k-major
+    timed(K_GEMM, st, [&] {
+      (void)gemm(operand(a, F, 1), operand(wd, F, 1), gemm_out(y + (int64_t)t0 * Dm, (int64_t)Dm), T, Dm, F, 0, st);
+    });
+    if (int rc = check_launch("MLP tile")) return rc;
+  }
+  return UPIPE_OK;
+}
+
+int run_mlp_bwd(const bf16* x, const bf16* wg, const bf16* wu, const bf16* wd, const bf16* dy, float* dx, float* dwg,
+                float* dwu, float* dwd, int S, int Dm, int F, int tile, char* ws, hipStream_t st) {
+  const MlpPool pool = mlp_pool(F, tile, true);
+  bf16* g = reinterpret_cast<bf16*>(ws + pool.g);  // becomes dg
+  bf16* u = reinterpret_cast<bf16*>(ws + pool.u);  // becomes du
+  const bf16* a = reinterpret_cast<const bf16*>(ws + pool.a);
+  float* da = reinterpret_cast<float*>(ws + pool.da);
+  for (int t0 = 0; t0 < S; t0 += tile) {
+    const int T = std::min(tile, S - t0);
+    // the tile's forward again (activations are not kept across the sequence)
+    if (int rc = mlp_tile_forward(x, wg, wu, t0, T, Dm, F, tile, pool, ws, true, st)) return rc;
+    const bf16* dyt = dy + (int64_t)t0 * Dm;
+    const bf16* xt = x + (int64_t)t0 * Dm;
+    // da = dy Wd: Wd read as [K = Dm][N = F], N contiguous
+    timed(K_GEMM, st, [&] {
+      (void)gemm(operand(dyt, Dm, 1), operand(wd, F, 0), gemm_out(da, (int64_t)F), T, F, Dm, 0, st);
+    });
+    timed(K_SWIGLU, st, [&] { hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(tile), dim3(256), 0, st, da, g, u, T, F); });
+    // dx = dg Wg + du Wu: Wg, Wu read as [K = F][N = Dm]
+    float* dxt = dx + (int64_t)t0 * Dm;
+    timed(K_GEMM, st, [&] {
+      (void)gemm(operand(g, F, 1), operand(wg, Dm, 0), gemm_out(dxt, (int64_t)Dm), T, Dm, F, 0, st);
+    });
+    timed(K_GEMM, st, [&] {
+      (void)gemm(operand(u, F, 1), operand(wu, Dm, 0), gemm_out(dxt, (int64_t)Dm), T, Dm, F, 1, st);
+    });
+    // weight gradients, summed over tiles in order: K = the tile's tokens,
+    // padded to the tile; the token-major x and dy rows past T are read as row
+    // T - 1 against the zero rows of dg, du and a
+    const GemmOperand xn = operand(xt, Dm, 0, kUnblocked, 0, T);     // [K = token][N = Dm]
+    const GemmOperand dym = operand(dyt, Dm, 0, kUnblocked, 0, T);   // [K = token][M = Dm]
+    timed(K_GEMM, st, [&] {
+      (void)gemm(operand(g, F, 0), xn, gemm_out(dwg, (int64_t)Dm), F, Dm, tile, t0 > 0, st);
+    });
+    timed(K_GEMM, st, [&] {
+      (void)gemm(operand(u, F, 0), xn, gemm_out(dwu, (int64_t)Dm), F, Dm, tile, t0 > 0, st);
+    });
+    timed(K_GEMM, st, [&] {
+      (void)gemm(dym, operand(a, F, 0), gemm_out(dwd, (int64_t)F), Dm, F, tile, t0 > 0, st);
+    });
+    if (int rc = check_launch("MLP backward tile")) return rc;
+  }
+  return UPIPE_OK;
+}
+
 }  // namespace
 }  // namespace upipe
 
@@ -929,6 +1036,52 @@ int upipe_ce_loss_tiled(const void* h, const void* w, const int32_t* labels, flo
   return run_ce_loss(reinterpret_cast<const bf16*>(h), reinterpret_cast<const bf16*>(w), labels, loss,
                      reinterpret_cast<bf16*>(dh), dw, S, Dm, V, tile, grad_scale, reinterpret_cast<char*>(workspace),
                      reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t upipe_mlp_workspace_bytes(int64_t S, int Dm, int F, int tile, int with_grad) {
+  if (validate_mlp(S, Dm, F, tile) != UPIPE_OK) return 0;
+  g_error.clear();
+  return mlp_pool(F, tile, with_grad != 0).total;
+}
+
+int upipe_mlp_tiled_fwd(const void* x, const void* wg, const void* wu, const void* wd, void* y, int64_t S, int Dm,
+                        int F, int tile, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = validate_mlp(S, Dm, F, tile)) return rc;
+  const void* ptrs[] = {x, wg, wu, wd, y, workspace};
+  const char* names[] = {"x", "wg", "wu", "wd", "y", "workspace"};
+  for (int i = 0; i < 6; ++i) {
+    if (!ptrs[i]) return fail(UPIPE_EINVAL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  const size_t need = mlp_pool(F, tile, false).total;
+  if (workspace_bytes < need)
+    return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  g_error.clear();
+  (void)hipGetLastError();
+  return run_mlp_fwd(reinterpret_cast<const bf16*>(x), reinterpret_cast<const bf16*>(wg),
+                     reinterpret_cast<const bf16*>(wu), reinterpret_cast<const bf16*>(wd), reinterpret_cast<bf16*>(y),
+                     (int)S, Dm, F, tile, reinterpret_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
+
+int upipe_mlp_tiled_bwd(const void* x, const void* wg, const void* wu, const void* wd, const void* dy, float* dx,
+                        float* dwg, float* dwu, float* dwd, int64_t S, int Dm, int F, int tile, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (int rc = validate_mlp(S, Dm, F, tile)) return rc;
+  const void* ptrs[] = {x, wg, wu, wd, dy, dx, dwg, dwu, dwd, workspace};
+  const char* names[] = {"x", "wg", "wu", "wd", "dy", "dx", "dwg", "dwu", "dwd", "workspace"};
+  for (int i = 0; i < 10; ++i) {
+    if (!ptrs[i]) return fail(UPIPE_EINVAL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  const size_t need = mlp_pool(F, tile, true).total;
+  if (workspace_bytes < need)
+    return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  g_error.clear();
+  (void)hipGetLastError();
+  return run_mlp_bwd(reinterpret_cast<const bf16*>(x), reinterpret_cast<const bf16*>(wg),
+                     reinterpret_cast<const bf16*>(wu), reinterpret_cast<const bf16*>(wd),
+                     reinterpret_cast<const bf16*>(dy), dx, dwg, dwu, dwd, (int)S, Dm, F, tile,
+                     reinterpret_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream));
 }
 
 int upipe_attn_plan(int Hq, int Hkv, int head_chunk, int max_chunks, int32_t* q_head0, int32_t* kv_head0,

@@ -17,3 +17,4 @@ from .attention import (  # noqa: F401
 )
 from .block import attention_block_forward, attention_block_rows, round_bf16  # noqa: F401,E402
 from .loss import cross_entropy  # noqa: F401,E402
+from .mlp import swiglu_mlp  # noqa: F401,E402

@@ -52,7 +52,7 @@ def errors(got, ref):
     return max_abs, rel
 
 
-def assert_close(name, got, ref, dtype, rel_only=False, grad_scale=1.0, per_item=False):
+def assert_close(name, got, ref, dtype, rel_only=False, grad_scale=1.0, per_item=False, elem_floor=1.0):
     """max |err| and relative Frobenius error of a tensor against the oracle.
 
     grad_scale: gradients are linear in dO, so for workloads whose dO is drawn
@@ -73,10 +73,25 @@ def assert_close(name, got, ref, dtype, rel_only=False, grad_scale=1.0, per_item
     if grad_scale != 1.0:
         # At unit dO scale gradient entries reach ~10 (a key's dV sums dO over
         # the rows that see it), where bf16's own half-ulp, 2^-8 |x|, exceeds
-        # 2e-2: the bound is absolute for |ref| <= 1 and relative above.
+        # 2e-2: the bound is absolute for |ref| <= floor and relative above.
+        # floor = 1, or (elem_floor="rms") the tensor's RMS at unit scale, for
+        # weight gradients summed over every token, whose rounding error grows
+        # with the size of the summed terms rather than with the sum.
+        # elem_floor="row": each item's (axis-0 row's) own RMS, for a gradient
+        # whose rows differ in scale by orders of magnitude (a vocabulary's
+        # rows: the labelled ones carry the one-hot term, the rest only
+        # softmax mass).
         g, r_ = got * grad_scale, ref * grad_scale
-        max_abs = float((np.abs(g - r_) / np.maximum(np.abs(r_), 1.0)).max()) if ref.size else 0.0
-        msg += f" max_err/max(|ref|,1)={max_abs:.3e}"
+        if elem_floor == "rms":
+            floor = float(np.sqrt(np.mean(r_ ** 2)))
+        elif elem_floor == "row":
+            n = r_.shape[0]
+            floor = np.sqrt(np.mean(r_.reshape(n, -1) ** 2, axis=1)).reshape((n,) + (1,) * (r_.ndim - 1))
+            floor = np.maximum(floor, 1e-30)
+        else:
+            floor = float(elem_floor)
+        max_abs = float((np.abs(g - r_) / np.maximum(np.abs(r_), floor)).max()) if ref.size else 0.0
+        msg += f" max_err/max(|ref|,{elem_floor})={max_abs:.3e}"
     worst = None
     if per_item and ref.shape[0] > 1:
         n = ref.shape[0]

@@ -533,3 +533,71 @@ def failing_ce_pins(lmod):
         except Exception:  # noqa: BLE001
             bad.append(pin.__name__)
     return bad
+
+
+
+# --- the sequence-tiled SwiGLU MLP ---------------------------------------------
+
+def pin_mlp_vs_torch(mmod, S=37, Dm=16, Fh=24):
+    """The MLP and its gradients against torch: F.linear, F.silu, the
+    bfloat16 conversion as the rounding step (wrapped so that its gradient
+    passes straight through in fp64), autograd for dx and the weight
+    gradients."""
+    x = _bf16_values((S, Dm), 91)
+    wg, wu = _bf16_values((Fh, Dm), 92, 0.4), _bf16_values((Fh, Dm), 93, 0.4)
+    wd = _bf16_values((Dm, Fh), 94, 0.4)
+    dy = _bf16_values((S, Dm), 95)
+    y, (dx, dwg, dwu, dwd) = mmod.swiglu_mlp(x, wg, wu, wd, dy)
+
+    class Rnd(torch.autograd.Function):
+        """bf16 rounding forward, identity backward (the gradient stays fp64)."""
+
+        @staticmethod
+        def forward(ctx, t):
+            return t.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+        @staticmethod
+        def backward(ctx, grad):
+            return grad
+
+    rnd = Rnd.apply
+    tx = torch.tensor(x, requires_grad=True)
+    tg, tu, td = (torch.tensor(w, requires_grad=True) for w in (wg, wu, wd))
+    g, u = rnd(F.linear(tx, tg)), rnd(F.linear(tx, tu))
+    ty = rnd(F.linear(rnd(F.silu(g) * u), td))
+    np.testing.assert_allclose(y, ty.detach().numpy(), rtol=0, atol=0)
+    ty.backward(torch.tensor(dy))
+    for got, ref in ((dx, tx.grad), (dwg, tg.grad), (dwu, tu.grad), (dwd, td.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def pin_mlp_closed_forms(mmod, S=9, Dm=8, Fh=16):
+    """Wu = 0: u = 0, so y = 0, and dWg = dx-from-g = 0 (du = da * silu(g)
+    remains); silu(0) = 0 makes Wg = 0 give y = 0 and du = 0."""
+    x = _bf16_values((S, Dm), 96)
+    w = _bf16_values((Fh, Dm), 97, 0.5)
+    wd = _bf16_values((Dm, Fh), 98, 0.5)
+    dy = _bf16_values((S, Dm), 99)
+    y, (dx, dwg, dwu, dwd) = mmod.swiglu_mlp(x, w, np.zeros((Fh, Dm)), wd, dy)
+    np.testing.assert_array_equal(y, 0.0)
+    np.testing.assert_array_equal(dwg, 0.0)
+    np.testing.assert_array_equal(dwd, 0.0)
+    assert np.abs(dwu).max() > 0
+    y, (dx, dwg, dwu, dwd) = mmod.swiglu_mlp(x, np.zeros((Fh, Dm)), w, wd, dy)
+    np.testing.assert_array_equal(y, 0.0)
+    np.testing.assert_array_equal(dwu, 0.0)
+    assert np.abs(dwg).max() > 0
+
+
+MLP_PINS = [pin_mlp_vs_torch, pin_mlp_closed_forms]
+
+
+def failing_mlp_pins(mmod):
+    bad = []
+    for pin in MLP_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mmod)
+        except Exception:  # noqa: BLE001
+            bad.append(pin.__name__)
+    return bad

@@ -340,3 +340,21 @@ def test_tiled_loss_host_checks():
     assert call(h=None) == -1 and "h is NULL" in L.upipe_last_error()
     assert call(ws=16) == -3
     assert call(S=0) == -1
+
+
+def test_tiled_mlp_host_checks():
+    lib = L.lib()
+    a = L.upipe_mlp_workspace_bytes(1 << 20, 4096, 14336, 4096, True)
+    assert a == L.upipe_mlp_workspace_bytes(5 << 20, 4096, 14336, 4096, True)  # independent of S
+    assert a >= 4096 * 14336 * (3 * 2 + 4)
+    assert L.upipe_mlp_workspace_bytes(1 << 20, 4096, 14336, 4096, False) < a
+    fwd = lambda **kw: lib.upipe_mlp_tiled_fwd(kw.get("x", FAKE), FAKE, FAKE, FAKE, FAKE, kw.get("S", 1000),  # noqa: E731
+                                               kw.get("Dm", 128), kw.get("F", 256), kw.get("tile", 128), FAKE,
+                                               kw.get("ws", 1 << 40), None)
+    assert fwd(F=100) == -2 and "multiple of 64" in L.upipe_last_error()
+    assert fwd(tile=96) == -1
+    assert fwd(x=None) == -1 and "x is NULL" in L.upipe_last_error()
+    assert fwd(ws=16) == -3
+    assert lib.upipe_mlp_tiled_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1000, 128, 256, 128, FAKE,
+                                   1 << 40, None) == -1
+    assert "dx is NULL" in L.upipe_last_error()

@@ -55,7 +55,7 @@ def test_tiled_cross_entropy_matches_oracle(S, Dm, V, tile, ignore_every):
     assert_close("loss", f64(loss), rl, "bf16", per_item=False)
     # gradients at unit upstream scale (x N), as for attention's dO
     assert_close("dh", f64(dh), rdh, "bf16", grad_scale=float(n), per_item=True)
-    assert_close("dw", f64(dw), rdw, "bf16", grad_scale=float(n), per_item=True)
+    assert_close("dw", f64(dw), rdw, "bf16", grad_scale=float(n), per_item=True, elem_floor="row")
     lf, _, _ = _run(h, w, labels, tile, scale, grad=False)
     assert bit_equal(lf, loss), "forward-only loss differs from the loss with gradients"
     if ignore_every:
