@@ -27,15 +27,28 @@ Readings where the pages are silent:
     block's intermediate q, k, v and o are the bf16 values a bf16 layer
     would hand on, i.e. each is the exact product rounded to float32 and then
     to bf16, round to nearest even (``round_bf16``); y is returned in fp64.
+
+The backward (:func:`attention_block_backward`) is the chain rule through the
+same steps, for the upstream gradient dy of y:
+
+    do_h   = dy Wo_h                     dWo_h = dy^T o_h
+    dq_h, dk_g, dv_g = attention backward (oracle.attention) from do
+    dx     = sum_h dq_h Wq_h + sum_g (dk_g Wk_g + dv_g Wv_g)
+    dWq_h  = dq_h^T x,  dWk_g = dk_g^T x,  dWv_g = dv_g^T x
+
+Reading for the backward: the forward's bf16 roundings are straight-through
+(their derivative is taken as 1) and the gradients themselves are kept exact
+in fp64; a bf16 layer would round do, dq, dk and dv once more, which the
+comparison's bf16 tolerance covers.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .attention import attention_forward, forward_rows
+from .attention import attention_backward, attention_forward, forward_rows
 
-__all__ = ["round_bf16", "attention_block_forward", "attention_block_rows"]
+__all__ = ["round_bf16", "attention_block_forward", "attention_block_rows", "attention_block_backward"]
 
 
 def round_bf16(x) -> np.ndarray:
@@ -81,3 +94,29 @@ def attention_block_rows(x, wq, wk, wv, wo, n_q_heads: int, n_kv_heads: int, row
     out, lse = forward_rows(q, k, v, rows, causal=causal)
     y = round_bf16(out).reshape(len(rows), n_q_heads * d) @ wo.T
     return y, out, lse
+
+
+def attention_block_backward(x, wq, wk, wv, wo, dy, n_q_heads: int, n_kv_heads: int, causal: bool = True,
+                             round_intermediates: bool = True):
+    """Gradients of sum(dy * y) for the block of :func:`attention_block_forward`
+    with respect to x and the four weights: (dx [S, Dm], dwq [Hq*d, Dm],
+    dwk, dwv [Hkv*d, Dm], dwo [Dm, Hq*d]), all fp64."""
+    x, wq, wk, wv, wo, dy = (np.asarray(t, dtype=np.float64) for t in (x, wq, wk, wv, wo, dy))
+    S, Dm = x.shape
+    d = wq.shape[0] // n_q_heads
+    rnd = round_bf16 if round_intermediates else (lambda t: t)
+    q = rnd(x @ wq.T).reshape(S, n_q_heads, d)
+    k = rnd(x @ wk.T).reshape(S, n_kv_heads, d)
+    v = rnd(x @ wv.T).reshape(S, n_kv_heads, d)
+    out, _ = attention_forward(q, k, v, causal=causal)
+    o = rnd(out).reshape(S, n_q_heads * d)
+    # y = o Wo^T: the gradient reaches o through Wo and Wo through o
+    dwo = dy.T @ o
+    do = (dy @ wo).reshape(S, n_q_heads, d)
+    dq, dk, dv = attention_backward(q, k, v, do, causal=causal)
+    dq = dq.reshape(S, n_q_heads * d)
+    dk = dk.reshape(S, n_kv_heads * d)
+    dv = dv.reshape(S, n_kv_heads * d)
+    # q = x Wq^T (and k, v likewise): x collects every projection's share
+    dx = dq @ wq + dk @ wk + dv @ wv
+    return dx, dq.T @ x, dk.T @ x, dv.T @ x, dwo

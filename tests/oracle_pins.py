@@ -472,8 +472,72 @@ def pin_block_rows(bmod, amod=None, S=41, Dm=16, Hq=4, Hkv=2, d=8):
         np.testing.assert_allclose(lser, lse[:, rows], rtol=1e-12, atol=1e-13)
 
 
+class _StraightThroughBf16(torch.autograd.Function):
+    """bf16 rounding forward, identity backward (the gradient stays fp64)."""
+
+    @staticmethod
+    def forward(ctx, t):
+        return t.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+    @staticmethod
+    def backward(ctx, grad):
+        return grad
+
+
+def _block_weights(S, Dm, Hq, Hkv, d, seed):
+    x = _bf16_values((S, Dm), seed)
+    wq, wk, wv = _bf16_values((Hq * d, Dm), seed + 1, 0.3), _bf16_values((Hkv * d, Dm), seed + 2, 0.3), \
+        _bf16_values((Hkv * d, Dm), seed + 3, 0.3)
+    wo = _bf16_values((Dm, Hq * d), seed + 4, 0.3)
+    dy = _bf16_values((S, Dm), seed + 5)
+    return x, wq, wk, wv, wo, dy
+
+
+def pin_block_backward_vs_torch(bmod, amod=None, S=31, Dm=24, Hq=4, Hkv=2, d=8):
+    """The block's gradients against torch autograd: F.linear projections,
+    fp64 SDPA with the kv heads repeated for GQA, the bfloat16 conversion as
+    the straight-through rounding of q, k, v and o; causal and not."""
+    x, wq, wk, wv, wo, dy = _block_weights(S, Dm, Hq, Hkv, d, 101)
+    rnd = _StraightThroughBf16.apply
+    for causal in (True, False):
+        grads = bmod.attention_block_backward(x, wq, wk, wv, wo, dy, Hq, Hkv, causal=causal)
+        tx, tq, tk, tv, to = (torch.tensor(t, requires_grad=True) for t in (x, wq, wk, wv, wo))
+        q = rnd(F.linear(tx, tq)).reshape(S, Hq, d).permute(1, 0, 2)
+        k = rnd(F.linear(tx, tk)).reshape(S, Hkv, d).permute(1, 0, 2)
+        v = rnd(F.linear(tx, tv)).reshape(S, Hkv, d).permute(1, 0, 2)
+        o = F.scaled_dot_product_attention(q.unsqueeze(0), k.repeat_interleave(Hq // Hkv, 0).unsqueeze(0),
+                                           v.repeat_interleave(Hq // Hkv, 0).unsqueeze(0), is_causal=causal)
+        y = F.linear(rnd(o.squeeze(0).permute(1, 0, 2).reshape(S, Hq * d)), to)
+        y.backward(torch.tensor(dy))
+        for got, ref in zip(grads, (tx.grad, tq.grad, tk.grad, tv.grad, to.grad)):
+            assert got.shape == tuple(ref.shape)
+            np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def pin_block_backward_finite_differences(bmod, amod=None, S=7, Dm=6, Hq=2, Hkv=1, d=3, eps=1e-5):
+    """Without the roundings the block is smooth: each gradient's inner
+    product with a random direction equals the central difference of
+    sum(dy * y) along it."""
+    x, wq, wk, wv, wo, dy = _block_weights(S, Dm, Hq, Hkv, d, 111)
+    params = [x, wq, wk, wv, wo]
+
+    def f(ps):
+        y = bmod.attention_block_forward(*ps, Hq, Hkv, round_intermediates=False)[0]
+        return float((dy * y).sum())
+
+    grads = bmod.attention_block_backward(*params, dy, Hq, Hkv, round_intermediates=False)
+    rng = np.random.default_rng(112)
+    for i, g in enumerate(grads):
+        e = rng.standard_normal(params[i].shape)
+        plus = [p + eps * e if j == i else p for j, p in enumerate(params)]
+        minus = [p - eps * e if j == i else p for j, p in enumerate(params)]
+        fd = (f(plus) - f(minus)) / (2 * eps)
+        np.testing.assert_allclose(float((g * e).sum()), fd, rtol=1e-6, atol=1e-9)
+
+
 BLOCK_PINS = [pin_round_bf16, pin_block_vs_torch, pin_block_identity_is_attention,
-              pin_block_linear_in_wo_and_head_order, pin_block_rows]
+              pin_block_linear_in_wo_and_head_order, pin_block_rows, pin_block_backward_vs_torch,
+              pin_block_backward_finite_differences]
 
 
 def failing_block_pins(bmod, amod):

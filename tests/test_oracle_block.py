@@ -33,6 +33,14 @@ MUTATIONS = {
                        "v = round_bf16(x @ wk.T).reshape(S, n_kv_heads, d)\n    q = round_bf16"),
     "non_causal": ("out, lse = attention_forward(q, k, v, causal=causal)",
                    "out, lse = attention_forward(q, k, v, causal=False)"),
+    "bwd_o_not_rounded": ("o = rnd(out).reshape(S, n_q_heads * d)", "o = out.reshape(S, n_q_heads * d)"),
+    "bwd_do_columns": ("do = (dy @ wo)", "do = (dy @ wo[:, ::-1])"),
+    "bwd_dwo_from_do": ("dwo = dy.T @ o", "dwo = dy.T @ (dy @ wo)"),
+    "bwd_dx_missing_dv": ("dx = dq @ wq + dk @ wk + dv @ wv", "dx = dq @ wq + dk @ wk"),
+    "bwd_dx_dk_through_wv": ("dx = dq @ wq + dk @ wk + dv @ wv", "dx = dq @ wq + dk @ wv + dv @ wv"),
+    "bwd_non_causal": ("dq, dk, dv = attention_backward(q, k, v, do, causal=causal)",
+                       "dq, dk, dv = attention_backward(q, k, v, do, causal=False)"),
+    "bwd_dwk_dwv_swapped": ("dq.T @ x, dk.T @ x, dv.T @ x", "dq.T @ x, dv.T @ x, dk.T @ x"),
 }
 
 
