@@ -303,8 +303,34 @@ def block_sweep(w, dev, chunks, warmup=1):
                      "pool_gib": round(ws.numel() / GIB, 4)})
         print(f"[bench] block fwd head_chunk={hc}: {ms:.1f} ms, peak {rows[-1]['peak_hbm_gib']:.2f} GiB",
               file=sys.stderr, flush=True)
-        del x, wq, wk, wv, wo, y, lse, ws
+        del y, lse, ws
+        # backward with o recomputed: x, weights, dy, the fp32 gradients and
+        # the pool; one timed call (its kernels are warm from the forward)
+        torch.cuda.synchronize(dev)
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev) - sum(t.numel() * t.element_size() for t in (x, wq, wk, wv, wo))
+        dy = torch.randn((w.S, Dm), generator=torch.Generator(device=dev).manual_seed(w.seed + 56), device=dev,
+                         dtype=torch.float32).to(torch.bfloat16)
+        grads = [torch.empty(t.shape, dtype=torch.float32, device=dev) for t in (x, wq, wk, wv, wo)]
+        ws = torch.empty(up.upipe_attn_block_bwd_workspace_bytes(w.S, Dm, w.Hq, w.Hkv, w.d, hc, True),
+                         dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        up.upipe_attn_block_bwd(x, wq, wk, wv, wo, dy, None, None, *grads, w.Hq, w.Hkv, hc, True, ws)
+        torch.cuda.synchronize(dev)
+        ms_b = (time.perf_counter() - t0) * 1e3
+        attn_b = 14 * w.d * w.Hq * pairs(w.S, True)  # forward again (4d) + backward (10d)
+        proj_b = 2 * w.S * Dm * w.d * (3 * (w.Hq + 2 * w.Hkv) + 2 * w.Hq)
+        rows[-1].update({"bwd_ms": round(ms_b, 2), "bwd_tflops": round((attn_b + proj_b) / (ms_b / 1e3) / 1e12, 2),
+                         "bwd_peak_hbm_gib": round((torch.cuda.max_memory_allocated(dev) - base) / GIB, 4),
+                         "bwd_pool_gib": round(ws.numel() / GIB, 4)})
+        print(f"[bench] block bwd head_chunk={hc}: {ms_b:.1f} ms, peak {rows[-1]['bwd_peak_hbm_gib']:.2f} GiB",
+              file=sys.stderr, flush=True)
+        del x, wq, wk, wv, wo, dy, grads, ws
     return {"Dm": Dm, "flops": "attention 4*d*Hq*S(S+1)/2 + projections 2*S*Dm*(Hq+2*Hkv)*d + 2*S*Hq*d*Dm",
+            "bwd": "o recomputed; attention 14*d*Hq*S(S+1)/2 (forward again + backward) + projections "
+                   "2*S*Dm*d*(3*(Hq+2*Hkv) + 2*Hq) (q, k, v again; dO; dWq, dWk, dWv; dx; dWo)",
             "sweep": rows}
 
 

@@ -274,6 +274,41 @@ int upipe_attn_block_fwd(const void* x, const void* wq, const void* wk, const vo
                          int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Attention block, backward, chunked around the heads like the forward (the
+ * same talk summary passages; the backward runs the chain rule through the
+ * forward's steps, each head chunk in ascending order through one pool).
+ * Per chunk:
+ *   q, k, v of its heads from x again (as the forward)
+ *   o: the caller's `out` rows, or (out == NULL) the chunk's attention
+ *      forward run again (the recomputation of activation checkpointing)
+ *   dO_h = dy Wo_h;  dWo_h = dy^T o_h
+ *   dq_h, dk_g, dv_g: the attention backward (as upipe_attn_bwd)
+ *   dWq_h = dq_h^T x;  dWk_g = dk_g^T x;  dWv_g = dv_g^T x
+ *   dx  += dq_h Wq_h (the chunk's heads of each kv group, in head order),
+ *          then dk_g Wk_g + dv_g Wv_g once group g's dk, dv are complete
+ *   x, wq, wk, wv, wo as upipe_attn_block_fwd; dy [S, Dm] bf16, the gradient
+ *       of y
+ *   out [S, Hq, d] bf16 and lse [Hq, S] fp32 from upipe_attn_block_fwd, or
+ *       out = NULL (lse is then not read and may be NULL)
+ *   dx [S, Dm], dwq [Hq*d, Dm], dwk, dwv [Hkv*d, Dm], dwo [Dm, Hq*d] fp32,
+ *       written (not accumulated into)
+ * q, k, v, o, dO, dq, dk and dv are bf16 in the pool; the weight gradients
+ * sum over tokens in one fixed order (64-token steps, the last one zero
+ * padded). Results are bit-identical across head_chunk. Workspace:
+ * upipe_attn_block_bwd_workspace_bytes(..., recompute) with recompute = 1 for
+ * out == NULL (it adds the transposed v, o's rounding residual and the lse
+ * rows); it rises with head_chunk only. Errors as upipe_attn_block_fwd; lse
+ * NULL with out given is UPIPE_EINVAL.
+ */
+size_t upipe_attn_block_bwd_workspace_bytes(int64_t S, int Dm, int Hq, int Hkv, int d,
+                                            int head_chunk, int recompute);
+int upipe_attn_block_bwd(const void* x, const void* wq, const void* wk, const void* wv,
+                         const void* wo, const void* dy, const void* out, const float* lse,
+                         float* dx, float* dwq, float* dwk, float* dwv, float* dwo,
+                         int64_t S, int Dm, int Hq, int Hkv, int d, int head_chunk,
+                         int causal, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Sequence-tiled cross-entropy over the vocabulary (talk summary, Chapters:
  * the sequence-tiling chapter -- the loss is computed in pieces along the
  * sequence so that the [S, V] logits never exist at once). Tiles of `tile`

@@ -11,6 +11,8 @@ from ._lib import (  # noqa: F401
     UPIPE_FP32,
     UpipeError,
     dtype_code,
+    upipe_attn_block_bwd,
+    upipe_attn_block_bwd_workspace_bytes,
     upipe_attn_block_fwd,
     upipe_attn_block_fwd_workspace_bytes,
     upipe_attn_bwd,

@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_block_fwd_workspace_bytes.restype = sz
     L.upipe_attn_block_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     L.upipe_attn_block_fwd.restype = i32
+    L.upipe_attn_block_bwd_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, i32]
+    L.upipe_attn_block_bwd_workspace_bytes.restype = sz
+    L.upipe_attn_block_bwd.argtypes = [vp] * 13 + [i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    L.upipe_attn_block_bwd.restype = i32
     L.upipe_ce_loss_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
     L.upipe_ce_loss_workspace_bytes.restype = sz
     L.upipe_ce_loss_tiled.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, ctypes.c_float, vp, sz, vp]
@@ -410,6 +414,50 @@ def upipe_attn_block_fwd(x, wq, wk, wv, wo, y, out, lse, n_q_heads, n_kv_heads, 
         _check(lib().upipe_attn_block_fwd(_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(y), _ptr(out),
                                           _ptr(lse), S, Dm, Hq, Hkv, d, int(head_chunk), int(causal),
                                           _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+
+
+def upipe_attn_block_bwd_workspace_bytes(S, Dm, Hq, Hkv, d, head_chunk, recompute=True) -> int:
+    n = lib().upipe_attn_block_bwd_workspace_bytes(S, Dm, Hq, Hkv, d, head_chunk, int(bool(recompute)))
+    if n == 0:
+        raise UpipeError(-1, upipe_last_error())
+    return n
+
+
+def upipe_attn_block_bwd(x, wq, wk, wv, wo, dy, out, lse, dx, dwq, dwk, dwv, dwo, n_q_heads, n_kv_heads, head_chunk,
+                         causal, workspace, stream=None) -> None:
+    """Attention block backward, chunk by chunk, for the upstream gradient dy
+    [S, Dm] bf16 of y: dx [S, Dm] and dwq, dwk, dwv, dwo (the weights'
+    shapes) fp32, written. out [S, Hq, d] bf16 and lse [Hq, S] fp32 from the
+    forward, or out = None to run the chunk's attention forward again (lse is
+    then not read)."""
+    if x.dim() != 2 or wq.dim() != 2:
+        raise UpipeError(-1, "x and the weights must be 2-D")
+    S, Dm = x.shape
+    Hq, Hkv = int(n_q_heads), int(n_kv_heads)
+    if wq.shape[0] % Hq:
+        raise UpipeError(-1, "wq's rows must be Hq * d")
+    d = wq.shape[0] // Hq
+    _require((x, wq, wk, wv, wo, dy) + ((out,) if out is not None else ()), torch.bfloat16)
+    _require((dx, dwq, dwk, dwv, dwo) + ((lse,) if out is not None else ()), torch.float32)
+    _require((workspace,), torch.uint8)
+    if out is None:
+        lse = None
+    for name, t, shape in (("wq", wq, (Hq * d, Dm)), ("wk", wk, (Hkv * d, Dm)), ("wv", wv, (Hkv * d, Dm)),
+                           ("wo", wo, (Dm, Hq * d)), ("dy", dy, (S, Dm)), ("out", out, (S, Hq, d)),
+                           ("lse", lse, (Hq, S)), ("dx", dx, (S, Dm)), ("dwq", dwq, (Hq * d, Dm)),
+                           ("dwk", dwk, (Hkv * d, Dm)), ("dwv", dwv, (Hkv * d, Dm)), ("dwo", dwo, (Dm, Hq * d)),
+                           ("workspace", workspace, (workspace.numel(),))):
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(shape):
+            raise UpipeError(-1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.device != x.device:
+            raise UpipeError(-1, f"{name} is on {t.device}, x on {x.device}")
+    with torch.cuda.device(x.device):
+        _check(lib().upipe_attn_block_bwd(_ptr(x), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(dy), _ptr(out),
+                                          _ptr(lse), _ptr(dx), _ptr(dwq), _ptr(dwk), _ptr(dwv), _ptr(dwo), S, Dm,
+                                          Hq, Hkv, d, int(head_chunk), int(causal), _ptr(workspace),
+                                          workspace.numel(), _stream_handle(stream)))
 
 
 def upipe_ce_loss_workspace_bytes(S, Dm, V, tile, with_grad=True) -> int:

@@ -11,7 +11,8 @@
 //    (plus its stored rounding residual when there is one; stored negated so
 //    the dK/dV kernel can start its dP accumulator from it), the
 //    chunk's dO rows packed, and lse_i * log2(e) (the base-2 exponent offset
-//    the backward kernels use), all in one pass.
+//    the backward kernels use), all in one pass;
+//  * tail_rows: a zero-padded copy of a matrix's last rows.
 #pragma once
 
 #include "common.hpp"
@@ -92,14 +93,24 @@ __global__ __launch_bounds__(256) void pack_vt_kernel(const bf16* __restrict__ s
   }
 }
 
+// Where bwd_pre finds the chunk's rows: element e of head hl at token i is
+// p[i * tok + hl * head + e] (the caller's token-major [S, H, d] at head h0:
+// tok = H*d, head = d; a head-major pool buffer [hc][S][d]: tok = d,
+// head = S*d).
+template <typename T>
+struct RowsView {
+  const T* p;
+  int64_t tok, head;
+};
+
 // One group of D/EPV lanes per (row, head): reads a 16-byte slice of out and
-// dout each, writes the dout slice into the pool, reduces the dot product.
+// dout each, copies the dout slice into the pool (if dout_pool is set),
+// reduces the dot product. lse: the chunk's natural-log rows, head stride S.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out, const T* __restrict__ out_lo,
-                                                     const T* __restrict__ dout,
+__global__ __launch_bounds__(256) void bwd_pre_kernel(RowsView<T> out, RowsView<T> out_lo, RowsView<T> dout,
                                                      const float* __restrict__ lse, T* __restrict__ dout_pool,
                                                      float* __restrict__ negD, float* __restrict__ lse2, int S,
-                                                     int H, int h0, int nh) {
+                                                     int nh) {
   constexpr int EPV = 16 / sizeof(T);
   constexpr int TPR = D / EPV;  // lanes per row: 16 (bf16, d=128), 8, 16 or 32
   constexpr int RPB = 256 / TPR;
@@ -112,11 +123,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
     const int64_t i = t0 + slot / nh;
     if (i >= S) break;
     const int hl = slot % nh;
-    const size_t src = ((size_t)i * H + h0 + hl) * D + sub * EPV;
-    const uint4 ov = *reinterpret_cast<const uint4*>(out + src);
-    const uint4 dv = *reinterpret_cast<const uint4*>(dout + src);
-    *reinterpret_cast<uint4*>(dout_pool + ((size_t)hl * S + i) * D + sub * EPV) = dv;
-    const uint4 lv = out_lo ? *reinterpret_cast<const uint4*>(out_lo + src) : uint4{0, 0, 0, 0};
+    const int e0 = sub * EPV;
+    const uint4 ov = *reinterpret_cast<const uint4*>(out.p + i * out.tok + hl * out.head + e0);
+    const uint4 dv = *reinterpret_cast<const uint4*>(dout.p + i * dout.tok + hl * dout.head + e0);
+    if (dout_pool) *reinterpret_cast<uint4*>(dout_pool + ((size_t)hl * S + i) * D + e0) = dv;
+    const uint4 lv = out_lo.p ? *reinterpret_cast<const uint4*>(out_lo.p + i * out_lo.tok + hl * out_lo.head + e0)
+                              : uint4{0, 0, 0, 0};
     const T* oe = reinterpret_cast<const T*>(&ov);
     const T* le = reinterpret_cast<const T*>(&lv);
     const T* de = reinterpret_cast<const T*>(&dv);
@@ -128,8 +140,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ out,
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
     if (sub == 0) {
       negD[(size_t)hl * S + i] = -acc;
-      lse2[(size_t)hl * S + i] = lse[(size_t)(h0 + hl) * S + i] * kLog2e;
+      lse2[(size_t)hl * S + i] = lse[(size_t)hl * S + i] * kLog2e;
     }
+  }
+}
+
+// dst [64][Dm] = rows 0 .. valid-1 of src [.][Dm], then zero rows: the last,
+// partial 64-deep K step of a GEMM that contracts over tokens (one operand
+// zero past the sequence end). One workgroup per row; Dm a multiple of 8.
+__global__ __launch_bounds__(256) void tail_rows_kernel(const bf16* __restrict__ src, bf16* __restrict__ dst,
+                                                       int valid, int Dm) {
+  const int r = blockIdx.x;
+  for (int j = threadIdx.x * 8; j < Dm; j += 256 * 8) {
+    const uint4 v = r < valid ? *reinterpret_cast<const uint4*>(src + (size_t)r * Dm + j) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(dst + (size_t)r * Dm + j) = v;
   }
 }
 

@@ -359,8 +359,12 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     const unsigned pre_grid =
         (unsigned)std::min<size_t>((rows + kRowsPerPreBlock - 1) / kRowsPerPreBlock, 256 * 32);
     timed(K_BWD_PRE, st, [&] {
-      hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st, (const T*)out, (const T*)out_lo, (const T*)dout, lse,
-                         dOc, nDc, L2c, S, pr.Hq, c.q_head0, pr.hc);
+      const int64_t tok = (int64_t)pr.Hq * D, h0 = (int64_t)c.q_head0 * D;  // caller's [S, Hq, d]
+      const RowsView<T> o_v{reinterpret_cast<const T*>(out) + h0, tok, D};
+      const RowsView<T> lo_v{out_lo ? reinterpret_cast<const T*>(out_lo) + h0 : nullptr, tok, D};
+      const RowsView<T> do_v{reinterpret_cast<const T*>(dout) + h0, tok, D};
+      hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3(pre_grid), dim3(256), 0, st, o_v, lo_v, do_v,
+                         lse + (size_t)c.q_head0 * S, dOc, nDc, L2c, S, pr.hc);
     });
 
     BwdParams<T> bp;
@@ -574,6 +578,249 @@ int run_block_fwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
       timed(K_GEMM, st, [&] { (void)gemm(oa, wob, yout, S, Dm, D, h > 0, st); });
     }
     if (int rc = check_launch("attention block chunk")) return rc;
+  }
+  return UPIPE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Attention block, backward. Pool: the chunk's q, o, dO and dq rows
+// (head-major), its kv heads' k and v rows (head-major) and their dk, dv rows
+// (token-major, as the dK/dV kernel writes them), -D and lse*log2(e) rows,
+// the fp32 dK/dV partials when chunks split a kv group, and the zero-padded
+// last rows of x and dy; when o is recomputed, also the transposed v, o's
+// rounding residual and the recomputed lse. Every chunk reuses the offsets.
+// ---------------------------------------------------------------------------
+struct BlockBwdPool {
+  size_t q, o, dout, dq, k, v, dk, dv, neg_d, lse2, dk_acc, dv_acc, xtail, dytail, vt, olo, lrec, total;
+  bool has_acc;
+};
+BlockBwdPool block_bwd_pool(const Problem& pr, int Dm, bool recompute) {
+  const size_t U = (size_t)pr.S * pr.d * 2;
+  const size_t R = (size_t)pr.hc * pr.S * 4;
+  BlockBwdPool p;
+  size_t off = 0;
+  p.q = off; off += align_up(pr.hc * U);
+  p.o = off; off += align_up(pr.hc * U);
+  p.dout = off; off += align_up(pr.hc * U);
+  p.dq = off; off += align_up(pr.hc * U);
+  p.k = off; off += align_up(pr.nkv * U);
+  p.v = off; off += align_up(pr.nkv * U);
+  p.dk = off; off += align_up(pr.nkv * U);
+  p.dv = off; off += align_up(pr.nkv * U);
+  p.neg_d = off; off += align_up(R);
+  p.lse2 = off; off += align_up(R);
+  p.has_acc = pr.hc < pr.G;
+  const size_t A = (size_t)pr.S * pr.d * 4;
+  p.dk_acc = off; off += p.has_acc ? align_up(A) : 0;
+  p.dv_acc = off; off += p.has_acc ? align_up(A) : 0;
+  p.xtail = off; off += align_up((size_t)64 * Dm * 2);
+  p.dytail = off; off += align_up((size_t)64 * Dm * 2);
+  p.vt = off; off += recompute ? align_up(pr.nkv * vt_bytes(pr)) : 0;
+  p.olo = off; off += recompute ? align_up(pr.hc * U) : 0;
+  p.lrec = off; off += recompute ? align_up(R) : 0;
+  p.total = off;
+  return p;
+}
+
+// C (+)= A B with K = S (a contraction over tokens) for A, B given as
+// [K = token][M or N] operands: the first K0 = S rounded down to 64 tokens
+// directly, the last S - K0 through the zero-padded copy `b_tail` of B's last
+// rows (A's rows past S are read as its last row, against those zeros).
+// `a_tail` is A advanced by K0 tokens.
+template <typename CT>
+int gemm_over_tokens(const GemmOperand& a, const GemmOperand& a_tail, const GemmOperand& b, const GemmOperand& b_tail,
+                     const GemmOut<CT>& c, int M, int N, int S, hipStream_t st) {
+  const int K0 = S / 64 * 64;
+  if (K0 > 0) timed(K_GEMM, st, [&] { (void)gemm(a, b, c, M, N, K0, 0, st); });
+  if (S > K0) timed(K_GEMM, st, [&] { (void)gemm(a_tail, b_tail, c, M, N, 64, K0 > 0, st); });
+  return check_launch("gemm over tokens");
+}
+
+template <int D>
+int run_block_bwd(const Problem& pr, int Dm, const void* x, const void* wq, const void* wk, const void* wv,
+                  const void* wo, const void* dy, const void* out, const float* lse, float* dx, float* dwq,
+                  float* dwk, float* dwv, float* dwo, char* ws, hipStream_t st) {
+  const bool recompute = out == nullptr;
+  const BlockBwdPool pool = block_bwd_pool(pr, Dm, recompute);
+  const int S = (int)pr.S;
+  const int64_t SD = (int64_t)S * D;
+  const int K0 = S / 64 * 64, tail = S - K0;
+  bf16* Qc = reinterpret_cast<bf16*>(ws + pool.q);
+  bf16* Oc = reinterpret_cast<bf16*>(ws + pool.o);
+  bf16* dOc = reinterpret_cast<bf16*>(ws + pool.dout);
+  bf16* dQc = reinterpret_cast<bf16*>(ws + pool.dq);
+  bf16* Kc = reinterpret_cast<bf16*>(ws + pool.k);
+  bf16* Vc = reinterpret_cast<bf16*>(ws + pool.v);
+  bf16* dKc = reinterpret_cast<bf16*>(ws + pool.dk);
+  bf16* dVc = reinterpret_cast<bf16*>(ws + pool.dv);
+  float* nDc = reinterpret_cast<float*>(ws + pool.neg_d);
+  float* L2c = reinterpret_cast<float*>(ws + pool.lse2);
+  float* dKa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dk_acc) : nullptr;
+  float* dVa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dv_acc) : nullptr;
+  bf16* xtail = reinterpret_cast<bf16*>(ws + pool.xtail);
+  bf16* dytail = reinterpret_cast<bf16*>(ws + pool.dytail);
+  bf16* Vt = recompute ? reinterpret_cast<bf16*>(ws + pool.vt) : nullptr;
+  bf16* OLc = recompute ? reinterpret_cast<bf16*>(ws + pool.olo) : nullptr;
+  float* Lrec = recompute ? reinterpret_cast<float*>(ws + pool.lrec) : nullptr;
+  const bf16* xb = reinterpret_cast<const bf16*>(x);
+  const bf16* dyb = reinterpret_cast<const bf16*>(dy);
+  const int n_fwd_tiles = (S + Bf16Tiles::kFwdRows - 1) / Bf16Tiles::kFwdRows;
+  const int n_qtiles = (S + Bf16Tiles::kDqRows - 1) / Bf16Tiles::kDqRows;
+  const int n_ktiles = (S + Bf16Tiles::kDkvKeys - 1) / Bf16Tiles::kDkvKeys;
+  const float scale = 1.0f / std::sqrt((float)D);
+  const GemmOperand xa = operand(x, Dm, 1);    // [S][Dm], K = Dm contiguous
+  const GemmOperand dya = operand(dy, Dm, 1);  // the same for dy
+  // x and dy as [K = token][N or M = Dm] operands, and their padded last rows
+  const GemmOperand x_tok = operand(x, Dm, 0), x_tail = operand(xtail, Dm, 0);
+  const GemmOperand dy_tok = operand(dy, Dm, 0), dy_tail = operand(dytail, Dm, 0);
+  if (tail > 0) {
+    timed(K_PACK, st, [&] {
+      hipLaunchKernelGGL(tail_rows_kernel, dim3(64), dim3(256), 0, st, xb + (int64_t)K0 * Dm, xtail, tail, Dm);
+    });
+    timed(K_PACK, st, [&] {
+      hipLaunchKernelGGL(tail_rows_kernel, dim3(64), dim3(256), 0, st, dyb + (int64_t)K0 * Dm, dytail, tail, Dm);
+    });
+  }
+  bool dx_started = false;
+  for (const Chunk& c : plan(pr)) {
+    if (c.load_kv) {
+      // k and v of the chunk's kv heads, head-major [nkv][S][D]
+      const GemmOperand wkb = operand(reinterpret_cast<const bf16*>(wk) + (int64_t)c.kv_head0 * D * Dm, Dm, 1);
+      const GemmOperand wvb = operand(reinterpret_cast<const bf16*>(wv) + (int64_t)c.kv_head0 * D * Dm, Dm, 1);
+      timed(K_GEMM, st, [&] { (void)gemm(xa, wkb, gemm_out(Kc, D, D, SD), S, c.n_kv * D, Dm, 0, st); });
+      timed(K_GEMM, st, [&] { (void)gemm(xa, wvb, gemm_out(Vc, D, D, SD), S, c.n_kv * D, Dm, 0, st); });
+      if (recompute)
+        for (int g = 0; g < c.n_kv; ++g)
+          timed(K_PACK, st, [&] {
+            hipLaunchKernelGGL((pack_vt_kernel<D>), dim3((unsigned)(vt_len(pr) / 64), 1), dim3(256), 0, st,
+                               Vc + g * SD, Vt + (int64_t)g * D * vt_len(pr), S, (int)vt_len(pr), 1, 0);
+          });
+    }
+    // q of the chunk's heads and dO = dy Wo (Wo's columns of those heads, as
+    // [K = Dm][N = hc*D]), both head-major [hc][S][D]
+    const GemmOperand wqb = operand(reinterpret_cast<const bf16*>(wq) + (int64_t)c.q_head0 * D * Dm, Dm, 1);
+    timed(K_GEMM, st, [&] { (void)gemm(xa, wqb, gemm_out(Qc, D, D, SD), S, pr.hc * D, Dm, 0, st); });
+    const GemmOperand wo_cols = operand(reinterpret_cast<const bf16*>(wo) + (int64_t)c.q_head0 * D, (int64_t)pr.Hq * D, 0);
+    timed(K_GEMM, st, [&] { (void)gemm(dya, wo_cols, gemm_out(dOc, D, D, SD), S, pr.hc * D, Dm, 0, st); });
+    // o of the chunk's heads: the caller's, or the forward run again
+    RowsView<bf16> lo_v{nullptr, 0, 0};
+    const float* lse_c;
+    if (recompute) {
+      FwdParams<bf16> fp;
+      fp.Sp = (int)vt_len(pr);
+      fp.q = Qc;
+      fp.k = Kc;
+      fp.v = Vt;
+      fp.o = Oc;
+      fp.o_lo = OLc;  // [S][hc][D]
+      fp.H = pr.hc;
+      fp.lse = Lrec;
+      fp.S = S;
+      fp.hc = pr.hc;
+      fp.heads_per_kv = pr.heads_per_kv;
+      fp.n_qtiles = n_fwd_tiles;
+      fp.causal = pr.causal;
+      fp.doc_off = nullptr;
+      fp.n_docs = 0;
+      fp.scale_log2 = scale * kLog2e;
+      timed(K_FWD, st, [&] {
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(n_fwd_tiles * pr.hc), dim3(256), 0, st, fp);
+      });
+      lo_v = RowsView<bf16>{OLc, (int64_t)pr.hc * D, D};
+      lse_c = Lrec;
+    } else {
+      const size_t nq = (size_t)S * pr.hc * (D / 8);
+      timed(K_PACK, st, [&] {
+        hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)out, (uint4*)Oc,
+                           S, pr.Hq, c.q_head0, pr.hc, D / 8);
+      });
+      lse_c = lse + (size_t)c.q_head0 * S;
+    }
+    constexpr int kRowsPerPreBlock = 256 / (D / 8);
+    const unsigned pre_grid =
+        (unsigned)std::min<size_t>(((size_t)S * pr.hc + kRowsPerPreBlock - 1) / kRowsPerPreBlock, 256 * 32);
+    timed(K_BWD_PRE, st, [&] {
+      hipLaunchKernelGGL((bwd_pre_kernel<bf16, D>), dim3(pre_grid), dim3(256), 0, st, RowsView<bf16>{Oc, D, SD},
+                         lo_v, RowsView<bf16>{dOc, D, SD}, lse_c, (bf16*)nullptr, nDc, L2c, S, pr.hc);
+    });
+    BwdParams<bf16> bp;
+    bp.q = Qc;
+    bp.k = Kc;
+    bp.v = Vc;
+    bp.dout = dOc;
+    bp.lse = lse_c;
+    bp.negD = nDc;
+    bp.lse2 = L2c;
+    bp.dq = dQc;
+    bp.dk_acc = dKa;
+    bp.dv_acc = dVa;
+    bp.dk_out = dKc;  // [S][nkv][D]
+    bp.dv_out = dVc;
+    bp.Hkv_total = c.n_kv;
+    bp.S = S;
+    bp.hc = pr.hc;
+    bp.heads_per_kv = pr.heads_per_kv;
+    bp.nkv = pr.nkv;
+    bp.n_qtiles = n_qtiles;
+    bp.n_ktiles = n_ktiles;
+    bp.causal = pr.causal;
+    bp.doc_off = nullptr;
+    bp.n_docs = 0;
+    bp.acc_load = !c.first_for_kv;
+    bp.finalize = c.last_for_kv;
+    bp.scale = scale;
+    bp.scale_log2 = scale * kLog2e;
+    timed(K_BWD_DKDV, st, [&] {
+      hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D>), dim3(n_ktiles * pr.nkv), dim3(256), 0, st, bp);
+    });
+    timed(K_BWD_DQ, st, [&] {
+      hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, bp);
+    });
+    if (int rc = check_launch("attention block backward chunk")) return rc;
+
+    // dWo's columns of the chunk's heads = dy^T o: [M = Dm][N = hc*D], K = tokens
+    const GemmOperand o_tok = operand(Oc, D, 0, D, SD), o_tail = operand(Oc + (int64_t)K0 * D, D, 0, D, SD, tail);
+    if (int rc = gemm_over_tokens(dy_tok, dy_tail, o_tok, o_tail, gemm_out(dwo + (int64_t)c.q_head0 * D,
+                                  (int64_t)pr.Hq * D), Dm, pr.hc * D, S, st))
+      return rc;
+    // dWq rows of the chunk's heads = dq^T x: [M = hc*D][N = Dm]
+    const GemmOperand dq_tok = operand(dQc, D, 0, D, SD), dq_tail = operand(dQc + (int64_t)K0 * D, D, 0, D, SD, tail);
+    if (int rc = gemm_over_tokens(dq_tok, dq_tail, x_tok, x_tail, gemm_out(dwq + (int64_t)c.q_head0 * D * Dm,
+                                  (int64_t)Dm), pr.hc * D, Dm, S, st))
+      return rc;
+    if (c.last_for_kv) {
+      const int64_t ldk = (int64_t)c.n_kv * D;  // dk, dv rows: [S][nkv][D]
+      const GemmOperand dk_tok = operand(dKc, ldk, 0), dk_tail = operand(dKc + K0 * ldk, ldk, 0, kUnblocked, 0, tail);
+      const GemmOperand dv_tok = operand(dVc, ldk, 0), dv_tail = operand(dVc + K0 * ldk, ldk, 0, kUnblocked, 0, tail);
+      if (int rc = gemm_over_tokens(dk_tok, dk_tail, x_tok, x_tail,
+                                    gemm_out(dwk + (int64_t)c.kv_head0 * D * Dm, (int64_t)Dm), c.n_kv * D, Dm, S, st))
+        return rc;
+      if (int rc = gemm_over_tokens(dv_tok, dv_tail, x_tok, x_tail,
+                                    gemm_out(dwv + (int64_t)c.kv_head0 * D * Dm, (int64_t)Dm), c.n_kv * D, Dm, S, st))
+        return rc;
+    }
+    // dx (+)= dq_h Wq_h for the chunk's heads of each kv group, then, once
+    // the group's dk and dv are final, dk_g Wk_g + dv_g Wv_g: one fixed order
+    // for every head_chunk, so dx's fp32 sums do not depend on it
+    GemmOut<float> dxo = gemm_out(dx, Dm);
+    const int groups = pr.hc >= pr.G ? c.n_kv : 1;
+    for (int gl = 0; gl < groups; ++gl) {
+      for (int j = 0; j < pr.heads_per_kv; ++j) {
+        const int hl = gl * pr.heads_per_kv + j, h = c.q_head0 + hl;
+        const GemmOperand wqh = operand(reinterpret_cast<const bf16*>(wq) + (int64_t)h * D * Dm, Dm, 0);
+        timed(K_GEMM, st, [&] { (void)gemm(operand(dQc + hl * SD, D, 1), wqh, dxo, S, Dm, D, dx_started, st); });
+        dx_started = true;
+      }
+      if (c.last_for_kv) {
+        const int64_t ldk = (int64_t)c.n_kv * D;
+        const int g = c.kv_head0 + gl;
+        const GemmOperand wkg = operand(reinterpret_cast<const bf16*>(wk) + (int64_t)g * D * Dm, Dm, 0);
+        const GemmOperand wvg = operand(reinterpret_cast<const bf16*>(wv) + (int64_t)g * D * Dm, Dm, 0);
+        timed(K_GEMM, st, [&] { (void)gemm(operand(dKc + gl * D, ldk, 1), wkg, dxo, S, Dm, D, 1, st); });
+        timed(K_GEMM, st, [&] { (void)gemm(operand(dVc + gl * D, ldk, 1), wvg, dxo, S, Dm, D, 1, st); });
+      }
+    }
+    if (int rc = check_launch("attention block backward projections")) return rc;
   }
   return UPIPE_OK;
 }
@@ -1009,6 +1256,40 @@ int upipe_attn_block_fwd(const void* x, const void* wq, const void* wk, const vo
   char* ws = reinterpret_cast<char*>(workspace);
   if (d == 128) return run_block_fwd<128>(pr, Dm, x, wq, wk, wv, wo, y, out, lse, ws, st);
   return run_block_fwd<64>(pr, Dm, x, wq, wk, wv, wo, y, out, lse, ws, st);
+}
+
+size_t upipe_attn_block_bwd_workspace_bytes(int64_t S, int Dm, int Hq, int Hkv, int d, int head_chunk,
+                                            int recompute) {
+  Problem pr;
+  if (validate_block(S, Dm, Hq, Hkv, d, head_chunk, 1, &pr) != UPIPE_OK) return 0;
+  g_error.clear();
+  return block_bwd_pool(pr, Dm, recompute != 0).total;
+}
+
+int upipe_attn_block_bwd(const void* x, const void* wq, const void* wk, const void* wv, const void* wo,
+                         const void* dy, const void* out, const float* lse, float* dx, float* dwq, float* dwk,
+                         float* dwv, float* dwo, int64_t S, int Dm, int Hq, int Hkv, int d, int head_chunk,
+                         int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  Problem pr;
+  if (int rc = validate_block(S, Dm, Hq, Hkv, d, head_chunk, causal, &pr)) return rc;
+  const void* ptrs[] = {x, wq, wk, wv, wo, dy, dx, dwq, dwk, dwv, dwo, workspace};
+  const char* names[] = {"x", "wq", "wk", "wv", "wo", "dy", "dx", "dwq", "dwk", "dwv", "dwo", "workspace"};
+  for (int i = 0; i < 12; ++i) {
+    if (!ptrs[i]) return fail(UPIPE_EINVAL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  if (out && !aligned16(out)) return fail(UPIPE_EINVAL, "out is not 16-byte aligned");
+  if (out && !lse) return fail(UPIPE_EINVAL, "lse is NULL (it is required when out is given)");
+  const size_t need = block_bwd_pool(pr, Dm, out == nullptr).total;
+  if (workspace_bytes < need)
+    return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  g_error.clear();
+  (void)hipGetLastError();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (d == 128)
+    return run_block_bwd<128>(pr, Dm, x, wq, wk, wv, wo, dy, out, lse, dx, dwq, dwk, dwv, dwo, ws, st);
+  return run_block_bwd<64>(pr, Dm, x, wq, wk, wv, wo, dy, out, lse, dx, dwq, dwk, dwv, dwo, ws, st);
 }
 
 size_t upipe_ce_loss_workspace_bytes(int64_t S, int Dm, int V, int tile, int with_grad) {

@@ -70,7 +70,7 @@ def assert_close(name, got, ref, dtype, rel_only=False, grad_scale=1.0, per_item
     max_abs, rel = errors(got * grad_scale, ref * grad_scale)
     msg = f"    {name:4s} max_abs={max_abs:.3e}" + (f" (x{grad_scale:.4g}, unit dO)" if grad_scale != 1.0 else "") \
         + f" rel_fro={rel:.3e}"
-    if grad_scale != 1.0:
+    if grad_scale != 1.0 or elem_floor != 1.0:
         # At unit dO scale gradient entries reach ~10 (a key's dV sums dO over
         # the rows that see it), where bf16's own half-ulp, 2^-8 |x|, exceeds
         # 2e-2: the bound is absolute for |ref| <= floor and relative above.
@@ -83,7 +83,9 @@ def assert_close(name, got, ref, dtype, rel_only=False, grad_scale=1.0, per_item
         # softmax mass).
         g, r_ = got * grad_scale, ref * grad_scale
         if elem_floor == "rms":
-            floor = float(np.sqrt(np.mean(r_ ** 2)))
+            # an all-zero reference (e.g. dq of a one-token sequence, where
+            # the only key takes softmax weight 1) keeps the absolute floor 1
+            floor = float(np.sqrt(np.mean(r_ ** 2))) or 1.0
         elif elem_floor == "row":
             n = r_.shape[0]
             floor = np.sqrt(np.mean(r_.reshape(n, -1) ** 2, axis=1)).reshape((n,) + (1,) * (r_.ndim - 1))

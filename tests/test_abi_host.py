@@ -311,6 +311,27 @@ def test_block_and_gemm_host_checks():
     assert blk(hc=3) == -1
     assert blk(ws=16) == -3
     assert blk(out=ctypes.c_void_p(0x10002)) == -1 and "out is not 16-byte aligned" in L.upipe_last_error()
+    # the backward's pool: more than the forward's, rises with head_chunk,
+    # and recomputing o adds the transposed v, o's residual and lse rows
+    bsz = [L.upipe_attn_block_bwd_workspace_bytes(S, Dm, Hq, Hkv, d, hc, True) for hc in (1, 2, 4)]
+    assert bsz[0] < bsz[1] < bsz[2] and bsz[0] > sizes[0]
+    kept = L.upipe_attn_block_bwd_workspace_bytes(S, Dm, Hq, Hkv, d, 1, False)
+    assert bsz[0] - kept >= 2 * U + S * 4  # transposed v, o residual, lse rows
+    assert lib.upipe_attn_block_bwd_workspace_bytes(S, 100, Hq, Hkv, d, 1, 1) == 0
+    names = ("x", "wq", "wk", "wv", "wo", "dy")
+    grads = ("dx", "dwq", "dwk", "dwv", "dwo")
+    bwd = lambda **kw: lib.upipe_attn_block_bwd(*(kw.get(n, FAKE) for n in names), kw.get("out"),  # noqa: E731
+                                                kw.get("lse"), *(kw.get(n, FAKE) for n in grads), S,
+                                                kw.get("Dm", Dm), Hq, Hkv, d, kw.get("hc", 1), 1, FAKE,
+                                                kw.get("ws", 1 << 40), None)
+    assert bwd(dy=None) == -1 and "dy is NULL" in L.upipe_last_error()
+    assert bwd(dwv=None) == -1 and "dwv is NULL" in L.upipe_last_error()
+    assert bwd(out=FAKE) == -1 and "lse is NULL" in L.upipe_last_error()
+    assert bwd(Dm=96) == -2
+    assert bwd(hc=3) == -1
+    assert bwd(ws=16) == -3 and "workspace too small" in L.upipe_last_error()
+    # recomputing o needs the larger pool: a pool sized without it is refused
+    assert bwd(ws=kept) == -3
     gemm = lambda M=64, N=64, K=64, lda=64, a_km=1, c_dtype=1, acc=0, a=FAKE: lib.upipe_gemm_bf16(  # noqa: E731
         a, lda, 0, 0, a_km, FAKE, K, 0, 0, 1, FAKE, N, 0, 0, c_dtype, acc, M, N, K, None)
     assert gemm(K=100) == -2 and "multiple of 64" in L.upipe_last_error()

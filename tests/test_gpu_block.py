@@ -1,6 +1,6 @@
 """The bf16 MFMA GEMM and the chunked attention block (q, k, v projections
-of each head chunk, attention, the chunk's share of the output projection)
-through the C ABI, against the oracle."""
+of each head chunk, attention, the chunk's share of the output projection;
+forward and backward) through the C ABI, against the oracle."""
 
 import math
 
@@ -11,7 +11,7 @@ import torch
 import long_context_attention_upipe_amd as up
 from gpu_util import OracleJobs, assert_close, bit_equal, f64, interleaved_parts
 from long_context_attention_upipe_amd.workloads import make_block_inputs, sample_rows
-from oracle.block import attention_block_forward, attention_block_rows
+from oracle.block import attention_block_backward, attention_block_forward, attention_block_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -171,3 +171,62 @@ def test_block_forward_128k_sampled_rows():
     assert pools[0] < pools[1] < pools[2]
     print(f"   pools (GiB) at head_chunk 1/2/4: {[round(p / 2 ** 30, 3) for p in pools]}", flush=True)
     assert math.isfinite(float(first[0].abs().max()))
+
+
+GRADS = ("dx", "dwq", "dwk", "dwv", "dwo")
+
+
+def _block_bwd_run(x, wq, wk, wv, wo, dy, Hq, Hkv, hc, causal=True, out=None, lse=None):
+    S, Dm = x.shape
+    d = wq.shape[0] // Hq
+    ws = torch.empty(up.upipe_attn_block_bwd_workspace_bytes(S, Dm, Hq, Hkv, d, hc, out is None),
+                     dtype=torch.uint8, device=x.device)
+    # NaN-filled outputs: an element the library does not write fails the check
+    res = [torch.full(t.shape, float("nan"), dtype=torch.float32, device=x.device) for t in (x, wq, wk, wv, wo)]
+    up.upipe_attn_block_bwd(x, wq, wk, wv, wo, dy, out, lse, *res, Hq, Hkv, hc, causal, ws)
+    torch.cuda.synchronize()
+    return res
+
+
+def _check_grads(got, refs):
+    """Element bounds: dx per token row (an early key's dk and dv sum over
+    every later row, so its token's dx row is far larger than the typical
+    one and carries proportionally larger bf16 rounding), the weight
+    gradients (sums over all tokens) against the tensor's RMS."""
+    for name, g, ref in zip(GRADS, got, refs):
+        assert_close(name, f64(g), ref, "bf16", per_item=True, elem_floor="row" if name == "dx" else "rms")
+
+
+@pytest.mark.parametrize("S,Dm,Hq,Hkv,d,hcs,causal", [
+    (1, 64, 2, 1, 64, (1, 2), True),
+    (300, 512, 4, 1, 128, (1, 2, 4), True),
+    (1000, 192, 8, 2, 64, (1, 2, 4, 8), True),
+    (517, 256, 4, 2, 128, (1, 4), False),
+    (8192, 256, 4, 1, 128, (1, 4), True),
+])
+def test_block_backward_full(S, Dm, Hq, Hkv, d, hcs, causal):
+    """dx and the four weight gradients against the oracle at every element,
+    with o recomputed (out = None) at each head_chunk (bit-identical across
+    them) and with the forward's out and lse handed over; the token
+    contraction's ragged last step (S not a multiple of 64) included."""
+    dev = _dev()
+    print(f"\n  block backward S={S} Dm={Dm} Hq={Hq} Hkv={Hkv} d={d} causal={causal} head_chunks={hcs}", flush=True)
+    x, wq, wk, wv, wo = make_block_inputs(S, Dm, Hq, Hkv, d, seed=60 + S, device=dev)
+    dy = _bf16((S, Dm), 61 + S, dev)
+    refs = attention_block_backward(*(f64(t) for t in (x, wq, wk, wv, wo, dy)), Hq, Hkv, causal=causal)
+    first = None
+    for hc in hcs:
+        print(f"   head_chunk={hc} (o recomputed)", flush=True)
+        r = _block_bwd_run(x, wq, wk, wv, wo, dy, Hq, Hkv, hc, causal)
+        _check_grads(r, refs)
+        if first is None:
+            first = r
+        else:
+            for name, a, b in zip(GRADS, r, first):
+                assert bit_equal(a, b), f"{name} differs between head_chunk {hcs[0]} and {hc}"
+    print(f"   head_chunk={hcs[-1]} (out and lse from the forward)", flush=True)
+    _, out, lse = _block_run(x, wq, wk, wv, wo, Hq, Hkv, hcs[-1], causal)
+    r = _block_bwd_run(x, wq, wk, wv, wo, dy, Hq, Hkv, hcs[-1], causal, out=out, lse=lse)
+    _check_grads(r, refs)
+    # dWo = dy^T o reads the same o bits either way
+    assert bit_equal(r[4], first[4]), "dwo differs between recomputed and handed-over o"
