@@ -26,6 +26,7 @@ namespace upipe {
 // kDkvKeys keys of each head), so a kernel and its launch cannot disagree.
 struct Bf16Tiles {
   static constexpr int kFwdRows = 128, kFwdKeys = 64;  // forward: rows per workgroup, keys per tile
+  static constexpr int kFwdPpRows = 256;               // the two-group forward's rows per workgroup
   static constexpr int kDqRows = 128, kDqKeys = 64;    // dQ: rows per workgroup, keys per tile
   static constexpr int kDkvKeys = 128, kDkvRows = 32;  // dK/dV: keys per workgroup, rows per step
 };
@@ -167,6 +168,262 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
     wait_vm();
     __syncthreads();
   }
+
+  const float l_tot = wave_xor32_sum(l_run);
+  if (my_row < S) {
+    const float inv = 1.f / l_tot;
+    bf16* O = p.o + (size_t)hl * head_elems + (size_t)my_row * D;
+    bf16* Olo = p.o_lo ? p.o_lo + ((size_t)my_row * p.H + hl) * D : nullptr;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        floatx4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = o_acc[db][jg * 4 + e] * inv;
+        const bf16x4 hi = to_out4(o4, bf16());
+        *reinterpret_cast<bf16x4*>(O + db * 32 + jg * 8 + half * 4) = hi;
+        if (Olo) {
+          const floatx4 r = o4 - __builtin_convertvector(hi, floatx4);
+          *reinterpret_cast<bf16x4*>(Olo + db * 32 + jg * 8 + half * 4) = to_out4(r, bf16());
+        }
+      }
+    if (half == 0) p.lse[(size_t)hl * S + my_row] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward, two wave groups one phase apart: 8 waves x 32 query rows (256 rows
+// per workgroup, one workgroup and two waves per SIMD on each CU). Each wave
+// runs, per key tile u, an MFMA phase (P V of tile u-1, then the scores of
+// tile u) and a softmax phase (mask, row max, rescale, exp, row sum, P to
+// bf16), each phase ending at a workgroup barrier. The waves of group 1 pass
+// one extra barrier before the tile loop (group 0 one after it), so on every
+// SIMD one wave's MFMAs run beside the other wave's softmax VALU work instead
+// of both waves reaching the same phase together. All waves run the same
+// code; only the position of the extra barrier depends on the group.
+// Per row, the operations are those of the 4-wave kernel above (rescale O,
+// then add P V, tile by tile); only the row sum of each tile is added in
+// four chains instead of one.
+// K of tile u lives in sK[u mod 3], V of tile u in sV[u mod 3].
+// Group 0 issues the copies of K(u+2) and V(u+1) at the start of its softmax
+// phase of tile u and waits for them at the end of its softmax phase of
+// u+1 (vmcnt leaving only the newer copies in flight), before the barrier
+// after which they are first read (its MFMA phase of u+2): two phases of
+// latency. The buffers it overwrites (K(u-1), V(u-2)) were last read in the
+// MFMA phases of u-1, before the barrier that ends the other group's. The
+// copies are untracked by the compiler (lds_copy16_untracked), so it keeps
+// counting the MFMA phases' LDS reads in order while they are in flight.
+// ---------------------------------------------------------------------------
+// Scheduling request for a block of N MFMAs that each use one LDS read: the
+// first AHEAD reads, then one MFMA and one read at a time, then the last
+// AHEAD MFMAs (instruction-scheduler groups; no effect on the results).
+template <int N, int AHEAD>
+__device__ __forceinline__ void mfma_ds_pipeline() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(FwdParams<bf16> p) {
+  constexpr int BQ = Bf16Tiles::kFwdPpRows, BK = Bf16Tiles::kFwdKeys, NKS = D / 16, NDB = D / 32;
+  static_assert(BQ == 8 * 32 && BK == 64, "8 waves x 32 rows; two 32-key blocks per tile");
+  __shared__ __attribute__((aligned(1024))) bf16 sK[3][BK * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[3][BK * D];
+  __shared__ int simd_waves[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Groups by SIMD: the first of the workgroup's waves on a SIMD (SIMD id
+  // from the HW_ID register) is in group 0, the second in group 1, so each
+  // SIMD holds one wave of each group; the copy slot of a group-0 wave is its
+  // SIMD. If the waves are not two per SIMD, groups fall back to waves 0-3
+  // and 4-7. Either way each group has four waves with distinct copy slots,
+  // so results never depend on the placement, only the overlap does.
+  if (tid < 4) simd_waves[tid] = 0;
+  __syncthreads();
+  const int simd = __builtin_amdgcn_s_getreg((4) | (4 << 6) | ((2 - 1) << 11)) & 3;  // HW_ID[5:4]
+  int slot = 0;
+  if (lane == 0) slot = atomicAdd(&simd_waves[simd], 1);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  __syncthreads();
+  const bool by_simd = simd_waves[0] == 2 && simd_waves[1] == 2 && simd_waves[2] == 2 && simd_waves[3] == 2;
+  const int grp = by_simd ? slot : wave >> 2;   // wave group
+  const int cw = by_simd ? simd : wave & 3;     // copy slot within group 0
+  const int col = lane & 31, half = lane >> 5;
+  const int S = p.S;
+
+  // XCD-aware order as in the 4-wave kernel.
+  const int t0 = blockIdx.x;
+  const int t = (t0 / 64 + 1) * 64 <= (int)gridDim.x ? (t0 & ~63) | ((t0 & 7) << 3) | ((t0 >> 3) & 7) : t0;
+  const int qt = p.causal ? (p.n_qtiles - 1 - t / p.hc) : (t / p.hc);
+  const int hl = t % p.hc;
+  const int kvl = hl / p.heads_per_kv;
+  const size_t head_elems = (size_t)S * D;
+  const bf16* __restrict__ Q = p.q + (size_t)hl * head_elems;
+  const bf16* __restrict__ K = p.k + (size_t)kvl * head_elems;
+  const bf16* __restrict__ VT = p.v + (size_t)kvl * D * p.Sp;
+
+  const int row0 = qt * BQ;
+  const int wrow0 = row0 + wave * 32;
+  const int my_row = wrow0 + col;
+
+  const int last_row = min(S, row0 + BQ) - 1;
+  const DocSpan kw = key_window(p.doc_off, p.n_docs, min(my_row, S - 1), S, p.causal);
+  const int w_first_min = __builtin_amdgcn_readlane(kw.first, 0);
+  const int w_first_max = __builtin_amdgcn_readlane(kw.first, 31);
+  const int w_last_min = __builtin_amdgcn_readlane(kw.last, 0);
+  const int w_last_max = __builtin_amdgcn_readlane(kw.last, 31);
+  const int kt_begin = p.doc_off ? key_window(p.doc_off, p.n_docs, row0, S, p.causal).first / BK : 0;
+  const int kt_end = key_window(p.doc_off, p.n_docs, last_row, S, p.causal).last / BK + 1;
+  const int n_t = kt_end - kt_begin;  // >= 1: a row always sees itself
+
+  // K(0), K(1) and V(0) before the loop; the loop's copies start with K(2), V(1)
+  tile_load_async<D, BK, 8, kSwzAll>(sK[0], K, kt_begin * BK, S, wave, lane);
+  if (n_t > 1) tile_load_async<D, BK, 8, kSwzAll>(sK[1], K, (kt_begin + 1) * BK, S, wave, lane);
+  tile_load_rows_async<BK, D, 8, kSwzAll>(sV[0], VT + (size_t)kt_begin * BK * D, BK, wave, lane);
+
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = my_row < S ? *reinterpret_cast<const bf16x8*>(Q + (size_t)my_row * D + ks * 16 + half * 8) : bf16x8{};
+
+  floatx16 o_acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o_acc[db] = floatx16{};
+  const float NEG_INF = -__builtin_inff();
+  float m_run = NEG_INF;
+  float l_run = 0.f;
+  floatx16 s[2];
+  bf16x8 pf[2][2];
+  bool s_act = false, p_act = false;
+
+  auto active = [&](int u) {
+    const int key0 = (kt_begin + u) * BK;
+    return (wrow0 < S) && key0 + BK - 1 >= w_first_min && key0 <= w_last_max;
+  };
+  // Barrier without a memory fence: LDS reads of the phase done, in-flight
+  // tile copies not waited for.
+  auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // One tile: MFMA phase, barrier, softmax phase, barrier.
+  // tile u: K(u) in sk, V(u-1) in sv_prev; copies go to sk_next (K(u+2))
+  // and sv_dst (V(u+1))
+  auto tile = [&](int u, const bf16* sk, const bf16* sv_prev, bf16* sk_next, bf16* sv_dst) {
+    // Each MFMA block reads its 16 fragments four MFMAs ahead of their use:
+    // in this phase no other wave's MFMAs fill the gaps of an LDS wait.
+    if (p_act) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            mma32(o_acc[db], tile_row_frag<BK, kSwzAll>(sv_prev, db * 32 + col, 4 * b + 2 * st + half), pf[b][st]);
+      mfma_ds_pipeline<16, 4>();
+    }
+    s_act = u < n_t && active(u);
+    if (s_act) {
+      // both 32-key blocks' accumulators live from the first MFMA on
+      s[0] = floatx16{};
+      s[1] = floatx16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          mma32(s[b], tile_row_frag<D, kSwzAll>(sk, b * 32 + col, 2 * ks + half), qf[ks]);
+      mfma_ds_pipeline<16, 4>();
+    }
+    barrier();
+    // copies of K(u+2) and V(u+1) by group 0, waited for in the next tile
+    const bool cp_k = u + 2 < n_t, cp_v = u + 1 < n_t;
+    if (grp == 0) {
+      if (cp_k) tile_load_untracked<D, BK, 4, kSwzAll>(sk_next, K, (kt_begin + u + 2) * BK, S, cw, lane);
+      if (cp_v)
+        tile_load_rows_untracked<BK, D, 4, kSwzAll>(sv_dst, VT + (size_t)(kt_begin + u + 1) * BK * D, BK, cw, lane);
+    }
+    if (s_act) {
+      const int key0 = (kt_begin + u) * BK;
+      const bool need_mask = key0 < w_first_max || key0 + BK - 1 > w_last_min;
+      if (need_mask) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int kb = key0 + b * 32 + half * 4;
+          const int lo = kw.first - kb, hi = kw.last - kb;
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (c_row(j, 0) < lo || c_row(j, 0) > hi) s[b][j] = NEG_INF;
+        }
+      }
+      // The softmax phase runs beside the other group's MFMAs with no other
+      // VALU work to fill its latencies: reductions go as independent chains,
+      // not one serial chain (the max is exact in any order).
+      float mx0 = NEG_INF, mx1 = NEG_INF;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        mx0 = fmaxf(mx0, s[0][j]);
+        mx1 = fmaxf(mx1, s[1][j]);
+      }
+      float mx = wave_xor32_max(fmaxf(mx0, mx1));
+      const float m_new = fmaxf(m_run, mx * p.scale_log2);
+      const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o_acc[db] *= alpha;
+      }
+      // row sum in four chains (registers j = 4c + e go to chain e), combined
+      // pairwise
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          s[b][j] = __builtin_amdgcn_exp2f(fmaf(s[b][j], p.scale_log2, -m_use));
+          ps[j & 3] += s[b][j];
+        }
+      l_run = l_run * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+      m_run = m_new;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          floatx8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = s[b][st * 8 + e];
+          pf[b][st] = to_frag(pv, bf16());
+        }
+    }
+    p_act = s_act;
+    // the previous tile's copies (issued one phase pair ago) complete; this
+    // tile's (4 per wave for K, 4 for V) may stay in flight. Group 1 has
+    // none, so the wait is free for it.
+    if (cp_k && cp_v)
+      wait_vm_leave<8>();
+    else if (cp_k || cp_v)
+      wait_vm_leave<4>();
+    else
+      wait_vm_leave<0>();
+    barrier();
+  };
+
+  wait_vm();
+  __syncthreads();
+  if (grp == 1) barrier();
+  // tiles u = 0 .. n_t (the last one only adds P V of tile n_t - 1)
+  int i0 = 0, i1 = 1, i2 = 2;  // u, u + 1, u + 2 mod 3
+  for (int u = 0; u <= n_t; ++u) {
+    tile(u, sK[i0], sV[i2], sK[i2], sV[i1]);
+    const int t_ = i0;
+    i0 = i1;
+    i1 = i2;
+    i2 = t_;
+  }
+  if (grp == 0) barrier();
 
   const float l_tot = wave_xor32_sum(l_run);
   if (my_row < S) {

@@ -129,6 +129,65 @@ __device__ __forceinline__ void tile_load_rows_async(bf16* tile, const bf16* g, 
   }
 }
 
+// One wave's 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4 of
+// base + lane offset, base uniform; LDS address from M0, which is saved and
+// restored), issued from inline assembly so that the compiler does not track
+// it: it then neither waits for it before LDS reads of other buffers nor
+// stops counting LDS reads in order while it is in flight. The caller orders
+// it by hand: s_waitcnt vmcnt (it counts these copies like any vector load)
+// and a barrier before the destination is read. Vector loads complete in
+// issue order, so a copy the compiler does not know of can only make its own
+// vmcnt waits stricter, never too short.
+__device__ __forceinline__ void lds_copy16_untracked(const void* base, unsigned byte_off, lds_void* l) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)l);
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_nop 0\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(byte_off), "s"(base), "s"(m0)
+               : "memory");
+}
+
+// tile_load_async / tile_load_rows_async through lds_copy16_untracked.
+template <int D, int ROWS, int NWAVES, int M = kSwzTr>
+__device__ __forceinline__ void tile_load_untracked(bf16* tile, const bf16* g, int g_row0, int S, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int INSTR = ROWS * CPR / 64;
+  static_assert(ROWS * CPR % 64 == 0 && INSTR % NWAVES == 0, "whole 1 KiB wave copies, split evenly");
+  const bf16* base = g + (size_t)g_row0 * D;
+  const int last = S - 1 - g_row0;  // rows past S - 1 repeat row S - 1
+#pragma unroll
+  for (int k = 0; k < INSTR / NWAVES; ++k) {
+    const int i = k * NWAVES + wave;
+    const int slot = i * 64 + lane;
+    const int r = slot / CPR, pos = slot % CPR;
+    const int c = pos ^ swz<D, M>(r);
+    lds_copy16_untracked(base, (unsigned)(min(r, last) * D + c * 8) * 2u, (lds_void*)(tile + i * 512));
+  }
+}
+template <int W, int ROWS, int NWAVES, int M = kSwzTr>
+__device__ __forceinline__ void tile_load_rows_untracked(bf16* tile, const bf16* g, int ld, int wave, int lane) {
+  constexpr int CPR = W / 8;
+  constexpr int INSTR = ROWS * CPR / 64;
+  static_assert(ROWS * CPR % 64 == 0 && INSTR % NWAVES == 0, "whole 1 KiB wave copies, split evenly");
+#pragma unroll
+  for (int k = 0; k < INSTR / NWAVES; ++k) {
+    const int i = k * NWAVES + wave;
+    const int slot = i * 64 + lane;
+    const int r = slot / CPR, pos = slot % CPR;
+    const int c = pos ^ swz<W, M>(r);
+    lds_copy16_untracked(g, (unsigned)(r * ld + c * 8) * 2u, (lds_void*)(tile + i * 512));
+  }
+}
+
+// Wait until at most N of this wave's vector loads (LDS copies included) are
+// outstanding; they complete in issue order. N in {0, 4, 8}.
+template <int N>
+__device__ __forceinline__ void wait_vm_leave() {
+  static_assert(N == 0 || N == 4 || N == 8, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // Wait for this wave's outstanding global loads (including LDS copies).
 __device__ __forceinline__ void wait_vm() {
   // s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima (no wait)

@@ -254,6 +254,19 @@ int check_launch(const char* what) {
   return UPIPE_OK;
 }
 
+// The bf16 forward: the two-group kernel (256 rows per workgroup) at d = 128,
+// the 4-wave kernel (128 rows) at d = 64. Sets fp.n_qtiles for the kernel.
+template <int D>
+void launch_attn_fwd_bf16(FwdParams<bf16> fp, hipStream_t st) {
+  if constexpr (D == 128) {
+    fp.n_qtiles = (fp.S + Bf16Tiles::kFwdPpRows - 1) / Bf16Tiles::kFwdPpRows;
+    hipLaunchKernelGGL((attn_fwd_bf16_pp_kernel<D>), dim3(fp.n_qtiles * fp.hc), dim3(512), 0, st, fp);
+  } else {
+    fp.n_qtiles = (fp.S + Bf16Tiles::kFwdRows - 1) / Bf16Tiles::kFwdRows;
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(fp.n_qtiles * fp.hc), dim3(256), 0, st, fp);
+  }
+}
+
 template <typename T, int D>
 int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* out, void* out_lo, float* lse,
             char* ws, hipStream_t st) {
@@ -306,7 +319,7 @@ int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void
     fp.scale_log2 = scale * kLog2e;
     timed(K_FWD, st, [&] {
       if constexpr (std::is_same<T, bf16>::value)
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, fp);
+        launch_attn_fwd_bf16<D>(fp, st);
       else
         hipLaunchKernelGGL((attn_fwd_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, fp);
     });
@@ -559,7 +572,7 @@ int run_block_fwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
     fp.n_docs = 0;
     fp.scale_log2 = scale * kLog2e;
     timed(K_FWD, st, [&] {
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, fp);
+      launch_attn_fwd_bf16<D>(fp, st);
     });
     if (out) {
       const size_t nq = (size_t)S * pr.hc * (D / 8);
@@ -724,7 +737,7 @@ int run_block_bwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
       fp.n_docs = 0;
       fp.scale_log2 = scale * kLog2e;
       timed(K_FWD, st, [&] {
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D>), dim3(n_fwd_tiles * pr.hc), dim3(256), 0, st, fp);
+        launch_attn_fwd_bf16<D>(fp, st);
       });
       lo_v = RowsView<bf16>{OLc, (int64_t)pr.hc * D, D};
       lse_c = Lrec;
