@@ -28,6 +28,7 @@ struct Bf16Tiles {
   static constexpr int kFwdRows = 128, kFwdKeys = 64;  // forward: rows per workgroup, keys per tile
   static constexpr int kFwdPpRows = 256;               // the two-group forward's rows per workgroup
   static constexpr int kDqRows = 128, kDqKeys = 64;    // dQ: rows per workgroup, keys per tile
+  static constexpr int kDqPpRows = 256, kDqPpKeys = 32;  // the two-group dQ: rows per workgroup, keys per tile
   static constexpr int kDkvKeys = 128, kDkvRows = 32;  // dK/dV: keys per workgroup, rows per step
 };
 
@@ -205,26 +206,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
 // Per row, the operations are those of the 4-wave kernel above (rescale O,
 // then add P V, tile by tile); only the row sum of each tile is added in
 // four chains instead of one.
-// K of tile u lives in sK[u mod 3], V of tile u in sV[u mod 3].
-// Group 0 issues the copies of K(u+2) and V(u+1) at the start of its softmax
-// phase of tile u and waits for them at the end of its softmax phase of
-// u+1 (vmcnt leaving only the newer copies in flight), before the barrier
-// after which they are first read (its MFMA phase of u+2): two phases of
-// latency. The buffers it overwrites (K(u-1), V(u-2)) were last read in the
-// MFMA phases of u-1, before the barrier that ends the other group's. The
-// copies are untracked by the compiler (lds_copy16_untracked), so it keeps
+// K of tile u lives in sK[u mod 3], V of tile u in sV[u mod 3]. Group 0
+// issues the copies of K(u+2) and V(u+1) at the start of its softmax phase
+// of tile u and waits for them at the end of its softmax phase of u+1
+// (vmcnt leaving only the newer copies in flight), before the barrier after
+// which they are first read (its MFMA phase of u+2): two phases of latency.
+// The buffers it overwrites (K(u-1), V(u-2)) were last read in the MFMA
+// phases of u-1, before the barrier that ends the other group's. The copies
+// are untracked by the compiler (lds_copy16x4_untracked), so it keeps
 // counting the MFMA phases' LDS reads in order while they are in flight.
 // ---------------------------------------------------------------------------
-// Scheduling request for a block of N MFMAs that each use one LDS read: the
-// first AHEAD reads, then one MFMA and one read at a time, then the last
-// AHEAD MFMAs (instruction-scheduler groups; no effect on the results).
-template <int N, int AHEAD>
+// Scheduling request for a block of N MFMAs that each use R LDS reads: the
+// reads of the first AHEAD MFMAs, then one MFMA and R reads at a time, then
+// the last AHEAD MFMAs (instruction-scheduler groups; no effect on the
+// results).
+template <int N, int AHEAD, int R = 1>
 __device__ __forceinline__ void mfma_ds_pipeline() {
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);  // DS reads
 #pragma unroll
   for (int i = 0; i < N - AHEAD; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // its R DS reads
   }
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(FwdParams<bf16
       mfma_ds_pipeline<16, 4>();
     }
     barrier();
-    // copies of K(u+2) and V(u+1) by group 0, waited for in the next tile
+    // the copies of K(u+2) and V(u+1), by group 0
     const bool cp_k = u + 2 < n_t, cp_v = u + 1 < n_t;
     if (grp == 0) {
       if (cp_k) tile_load_untracked<D, BK, 4, kSwzAll>(sk_next, K, (kt_begin + u + 2) * BK, S, cw, lane);
@@ -399,15 +401,16 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_pp_kernel(FwdParams<bf16
         }
     }
     p_act = s_act;
-    // the previous tile's copies (issued one phase pair ago) complete; this
-    // tile's (4 per wave for K, 4 for V) may stay in flight. Group 1 has
-    // none, so the wait is free for it.
-    if (cp_k && cp_v)
-      wait_vm_leave<8>();
-    else if (cp_k || cp_v)
-      wait_vm_leave<4>();
-    else
-      wait_vm_leave<0>();
+    // the previous tile's copies complete; this tile's (4 per wave for K,
+    // 4 for V) may stay in flight. Group 1 has none.
+    if (grp == 0) {
+      if (cp_k && cp_v)
+        wait_vm_leave<8>();
+      else if (cp_k || cp_v)
+        wait_vm_leave<4>();
+      else
+        wait_vm_leave<0>();
+    }
     barrier();
   };
 
@@ -583,6 +586,201 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(BwdParams<bf16
 }
 
 // ---------------------------------------------------------------------------
+// dQ, two wave groups one phase apart (the scheme of the two-group forward):
+// 8 waves x 32 query rows, 256 rows per workgroup, key tiles of 32 (one
+// block per phase keeps the scores, dP - D and dS of a tile within the
+// register budget). Per key tile u, the MFMA phase adds dS(u-1) K(u-1) to
+// dQ and forms the scores and dP - D of tile u; the softmax phase turns them
+// into dS(u) = P (dP - D) in bf16. dQ receives the same products in the same
+// order as in the 4-wave kernel above (16-key steps in key order), so
+// results are identical.
+// K of tile u lives in sK[u mod 4] (it is read again, transposed, in the MFMA
+// phase of u+1), V of tile u in sV[u mod 3]. In its softmax phase of u, group
+// 0 copies K(u+2) (its waves 0-1) and V(u+2) (waves 2-3) and waits for them
+// at the end of its softmax phase of u+1; they are first read in its MFMA
+// phase of u+2. The buffers they overwrite (K(u-2), V(u-1)) were last read in
+// the MFMA phases of u-1. The copies are untracked (lds_copy16x4_untracked).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_bf16_pp_kernel(BwdParams<bf16> p) {
+  constexpr int BQ = Bf16Tiles::kDqPpRows, BK = Bf16Tiles::kDqPpKeys, NKS = D / 16, NDB = D / 32;
+  static_assert(BQ == 8 * 32 && BK == 32, "8 waves x 32 rows; one 32-key block per tile");
+  __shared__ __attribute__((aligned(1024))) bf16 sK[4][BK * D];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[3][BK * D];
+  __shared__ int simd_waves[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // wave groups by SIMD, as in the two-group forward
+  if (tid < 4) simd_waves[tid] = 0;
+  __syncthreads();
+  const int simd = __builtin_amdgcn_s_getreg((4) | (4 << 6) | ((2 - 1) << 11)) & 3;  // HW_ID[5:4]
+  int slot = 0;
+  if (lane == 0) slot = atomicAdd(&simd_waves[simd], 1);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  __syncthreads();
+  const bool by_simd = simd_waves[0] == 2 && simd_waves[1] == 2 && simd_waves[2] == 2 && simd_waves[3] == 2;
+  const int grp = by_simd ? slot : wave >> 2;
+  const int cw = by_simd ? simd : wave & 3;
+  const int col = lane & 31, half = lane >> 5;
+  const int S = p.S;
+
+  const int t0 = blockIdx.x;
+  const int t = (t0 / 64 + 1) * 64 <= (int)gridDim.x ? (t0 & ~63) | ((t0 & 7) << 3) | ((t0 >> 3) & 7) : t0;
+  const int qt = p.causal ? (p.n_qtiles - 1 - t / p.hc) : (t / p.hc);
+  const int hl = t % p.hc;
+  const int kvl = hl / p.heads_per_kv;
+  const size_t head_elems = (size_t)S * D;
+  const bf16* __restrict__ Q = p.q + (size_t)hl * head_elems;
+  const bf16* __restrict__ dO = p.dout + (size_t)hl * head_elems;
+  const bf16* __restrict__ K = p.k + (size_t)kvl * head_elems;
+  const bf16* __restrict__ V = p.v + (size_t)kvl * head_elems;
+
+  const int row0 = qt * BQ;
+  const int wrow0 = row0 + wave * 32;
+  const int my_row = wrow0 + col;
+  const bool row_ok = my_row < S;
+
+  const int last_row = min(S, row0 + BQ) - 1;
+  const DocSpan kw = key_window(p.doc_off, p.n_docs, min(my_row, S - 1), S, p.causal);
+  const int w_first_min = __builtin_amdgcn_readlane(kw.first, 0);
+  const int w_first_max = __builtin_amdgcn_readlane(kw.first, 31);
+  const int w_last_min = __builtin_amdgcn_readlane(kw.last, 0);
+  const int w_last_max = __builtin_amdgcn_readlane(kw.last, 31);
+  const int kt_begin = p.doc_off ? key_window(p.doc_off, p.n_docs, row0, S, p.causal).first / BK : 0;
+  const int kt_end = key_window(p.doc_off, p.n_docs, last_row, S, p.causal).last / BK + 1;
+  const int n_t = kt_end - kt_begin;
+
+  // K(0), V(0), K(1), V(1) before the loop; the loop's copies start with tile 2
+  tile_load_async<D, BK, 8>(sK[0], K, kt_begin * BK, S, wave, lane);
+  tile_load_async<D, BK, 8>(sV[0], V, kt_begin * BK, S, wave, lane);
+  if (n_t > 1) {
+    tile_load_async<D, BK, 8>(sK[1], K, (kt_begin + 1) * BK, S, wave, lane);
+    tile_load_async<D, BK, 8>(sV[1], V, (kt_begin + 1) * BK, S, wave, lane);
+  }
+
+  bf16x8 qf[NKS], df[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qf[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(Q + (size_t)my_row * D + ks * 16 + half * 8) : bf16x8{};
+    df[ks] = row_ok ? *reinterpret_cast<const bf16x8*>(dO + (size_t)my_row * D + ks * 16 + half * 8) : bf16x8{};
+  }
+  const float l2 = row_ok ? p.lse2[(size_t)hl * S + my_row] : 0.f;
+  const float nD = row_ok ? p.negD[(size_t)hl * S + my_row] : 0.f;
+
+  floatx16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = floatx16{};
+  floatx16 s, dp;
+  bf16x8 dsf[2];
+  bool s_act = false, ds_act = false;
+
+  auto active = [&](int u) {
+    const int key0 = (kt_begin + u) * BK;
+    return (wrow0 < S) && key0 + BK - 1 >= w_first_min && key0 <= w_last_max;
+  };
+  auto barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  // tile u: K(u) in sk, K(u-1) in sk_prev, V(u) in sv; copies of K(u+2), V(u+2)
+  // go to sk_dst, sv_dst
+  auto tile = [&](int u, const bf16* sk, const bf16* sk_prev, const bf16* sv, bf16* sk_dst, bf16* sv_dst) {
+    if (ds_act) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          mma32(acc[db], tile_tr_frag<D>(sk_prev, st * 16, db * 32, lane), dsf[st]);
+      mfma_ds_pipeline<8, 2, 2>();
+    }
+    s_act = u < n_t && active(u);
+    if (s_act) {
+      // dP starts from this lane's row -D, so the MFMAs yield dP - D
+      s = floatx16{};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dp[j] = nD;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        mma32(s, tile_row_frag<D>(sk, col, 2 * ks + half), qf[ks]);
+        mma32(dp, tile_row_frag<D>(sv, col, 2 * ks + half), df[ks]);
+      }
+      mfma_ds_pipeline<16, 4>();
+    }
+    barrier();
+    const bool cp = u + 2 < n_t;
+    if (grp == 0 && cp) {
+      if (cw < 2)
+        tile_load_untracked<D, BK, 2>(sk_dst, K, (kt_begin + u + 2) * BK, S, cw, lane);
+      else
+        tile_load_untracked<D, BK, 2>(sv_dst, V, (kt_begin + u + 2) * BK, S, cw - 2, lane);
+    }
+    if (s_act) {
+      const int key0 = (kt_begin + u) * BK;
+      const bool need_mask = key0 < w_first_max || key0 + BK - 1 > w_last_min;
+      if (need_mask) {
+        const int kb = key0 + half * 4;
+        const int lo = kw.first - kb, hi = kw.last - kb;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kj = c_row(j, 0);
+          const float pij = (kj >= lo && kj <= hi) ? __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2)) : 0.f;
+          s[j] = pij * dp[j];  // dS^T = P (dP - D)
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float pij = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -l2));
+          s[j] = pij * dp[j];
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        floatx8 d8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d8[e] = s[st * 8 + e];
+        dsf[st] = to_frag(d8, bf16());
+      }
+    }
+    ds_act = s_act;
+    // the previous tile's copies complete; this tile's (4 per wave) may stay
+    // in flight. Group 1 has none.
+    if (grp == 0) {
+      if (cp)
+        wait_vm_leave<4>();
+      else
+        wait_vm_leave<0>();
+    }
+    barrier();
+  };
+
+  wait_vm();
+  __syncthreads();
+  if (grp == 1) barrier();
+  int k0 = 0, k3 = 3, k2 = 2;  // u, u - 1, u + 2 mod 4
+  int v0 = 0, v2 = 2;          // u, u + 2 mod 3
+  for (int u = 0; u <= n_t; ++u) {
+    tile(u, sK[k0], sK[k3], sV[v0], sK[k2], sV[v2]);
+    k3 = k0;
+    k0 = (k0 + 1) & 3;
+    k2 = (k2 + 1) & 3;
+    v0 = v0 == 2 ? 0 : v0 + 1;
+    v2 = v2 == 2 ? 0 : v2 + 1;
+  }
+  if (grp == 0) barrier();
+
+  if (row_ok) {
+    bf16* dQ = p.dq + (size_t)hl * head_elems + (size_t)my_row * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        floatx4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[db][jg * 4 + e] * p.scale;
+        *reinterpret_cast<bf16x4*>(dQ + db * 32 + jg * 8 + half * 4) = to_out4(v4, bf16());
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dK/dV: 4 waves x 32 keys; query rows in steps of 32, head-major, each head's
 // row blocks from the last one down to the workgroup's diagonal. Workgroups
 // resident together then read the same Q/dO block at about the same time, so
@@ -645,15 +843,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
       --qb;
     }
   };
+  // The step copies are untracked (lds_copy16x2_untracked): the compiler
+  // would otherwise wait for the next step's copies before the first LDS
+  // read of the current step. They are waited for at the end of the step.
   auto issue = [&](int hi, int qb, int buf) {
     const int hl = g * p.heads_per_kv + hi;
     const int r0 = qb * BQ;
-    tile_load_async<D, BQ, 4, kSwzAll>(sQ[buf], p.q + (size_t)hl * head_elems, r0, S, wave, lane);
-    tile_load_async<D, BQ, 4, kSwzAll>(sO[buf], p.dout + (size_t)hl * head_elems, r0, S, wave, lane);
+    tile_load_untracked<D, BQ, 4, kSwzAll>(sQ[buf], p.q + (size_t)hl * head_elems, r0, S, wave, lane);
+    tile_load_untracked<D, BQ, 4, kSwzAll>(sO[buf], p.dout + (size_t)hl * head_elems, r0, S, wave, lane);
     if (wave == 0) {
       const int r = min(r0 + (lane & 31), S - 1);
       const float* src = (lane < 32 ? p.lse2 : p.negD) + (size_t)hl * S + r;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)&sLD[buf][0], 4, 0, 0);
+      lds_copy4_untracked((const void*)src, (lds_void*)&sLD[buf][0]);
     }
   };
 

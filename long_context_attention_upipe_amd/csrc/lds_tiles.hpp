@@ -129,55 +129,108 @@ __device__ __forceinline__ void tile_load_rows_async(bf16* tile, const bf16* g, 
   }
 }
 
-// One wave's 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4 of
-// base + lane offset, base uniform; LDS address from M0, which is saved and
-// restored), issued from inline assembly so that the compiler does not track
-// it: it then neither waits for it before LDS reads of other buffers nor
-// stops counting LDS reads in order while it is in flight. The caller orders
-// it by hand: s_waitcnt vmcnt (it counts these copies like any vector load)
-// and a barrier before the destination is read. Vector loads complete in
-// issue order, so a copy the compiler does not know of can only make its own
-// vmcnt waits stricter, never too short.
-__device__ __forceinline__ void lds_copy16_untracked(const void* base, unsigned byte_off, lds_void* l) {
+// Four of one wave's 16-byte-per-lane global -> LDS copies
+// (global_load_lds_dwordx4 of base + the lane's offset o[k], base uniform),
+// to LDS addresses l, l + step, l + 2 step, l + 3 step (bytes; the LDS address
+// goes in M0, which is saved and restored), issued from inline assembly so
+// that the compiler does not track them: it then neither waits for them
+// before LDS reads of other buffers nor stops counting LDS reads in order
+// while they are in flight. The caller orders them by hand: s_waitcnt vmcnt
+// (they count like any vector load) and a barrier before the destination is
+// read. Vector loads complete in issue order, so copies the compiler does
+// not know of can only make its own vmcnt waits stricter, never too short.
+template <unsigned STEP>
+__device__ __forceinline__ void lds_copy16x4_untracked(const void* base, unsigned o0, unsigned o1, unsigned o2,
+                                                       unsigned o3, lds_void* l) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)l);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %5\n\t"
+      "s_add_u32 m0, m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %5\n\t"
+      "s_add_u32 m0, m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %5\n\t"
+      "s_add_u32 m0, m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, %5\n\t"
+      "s_nop 0\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o0), "v"(o1), "v"(o2), "v"(o3), "s"(base), "s"(m0), "i"(STEP)
+      : "memory", "scc");
+}
+
+// The same with two copies (l, l + step).
+template <unsigned STEP>
+__device__ __forceinline__ void lds_copy16x2_untracked(const void* base, unsigned o0, unsigned o1, lds_void* l) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)l);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %3\n\t"
+      "s_add_u32 m0, m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+      "s_nop 0\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(o0), "v"(o1), "s"(base), "s"(m0), "i"(STEP)
+      : "memory", "scc");
+}
+
+// The same with one copy.
+__device__ __forceinline__ void lds_copy16x1_untracked(const void* base, unsigned o0, lds_void* l) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)l);
   unsigned saved;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_nop 0\n\t"
                "s_mov_b32 m0, %0"
                : "=&s"(saved)
-               : "v"(byte_off), "s"(base), "s"(m0)
+               : "v"(o0), "s"(base), "s"(m0)
                : "memory");
 }
 
-// tile_load_async / tile_load_rows_async through lds_copy16_untracked.
+// One 4-byte-per-lane copy from a per-lane 64-bit address, untracked like
+// the above.
+__device__ __forceinline__ void lds_copy4_untracked(const void* g, lds_void* l) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)l);
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_nop 0\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(g), "s"(m0)
+               : "memory");
+}
+
+// tile_load_async / tile_load_rows_async through the untracked copies, for
+// tiles that take one, two or four wave copies per wave.
 template <int D, int ROWS, int NWAVES, int M = kSwzTr>
 __device__ __forceinline__ void tile_load_untracked(bf16* tile, const bf16* g, int g_row0, int S, int wave, int lane) {
   constexpr int CPR = D / 8;
-  constexpr int INSTR = ROWS * CPR / 64;
-  static_assert(ROWS * CPR % 64 == 0 && INSTR % NWAVES == 0, "whole 1 KiB wave copies, split evenly");
+  constexpr int PER = ROWS * CPR / (64 * NWAVES);
+  static_assert(ROWS * CPR == PER * 64 * NWAVES && (PER == 1 || PER == 2 || PER == 4), "1, 2 or 4 wave copies per wave");
   const bf16* base = g + (size_t)g_row0 * D;
   const int last = S - 1 - g_row0;  // rows past S - 1 repeat row S - 1
+  unsigned o[PER];
 #pragma unroll
-  for (int k = 0; k < INSTR / NWAVES; ++k) {
-    const int i = k * NWAVES + wave;
-    const int slot = i * 64 + lane;
+  for (int k = 0; k < PER; ++k) {
+    const int slot = (k * NWAVES + wave) * 64 + lane;
     const int r = slot / CPR, pos = slot % CPR;
     const int c = pos ^ swz<D, M>(r);
-    lds_copy16_untracked(base, (unsigned)(min(r, last) * D + c * 8) * 2u, (lds_void*)(tile + i * 512));
+    o[k] = (unsigned)(min(r, last) * D + c * 8) * 2u;
   }
+  if constexpr (PER == 4)
+    lds_copy16x4_untracked<NWAVES * 1024>(base, o[0], o[1], o[2], o[3], (lds_void*)(tile + wave * 512));
+  else if constexpr (PER == 2)
+    lds_copy16x2_untracked<NWAVES * 1024>(base, o[0], o[1], (lds_void*)(tile + wave * 512));
+  else
+    lds_copy16x1_untracked(base, o[0], (lds_void*)(tile + wave * 512));
 }
 template <int W, int ROWS, int NWAVES, int M = kSwzTr>
 __device__ __forceinline__ void tile_load_rows_untracked(bf16* tile, const bf16* g, int ld, int wave, int lane) {
   constexpr int CPR = W / 8;
-  constexpr int INSTR = ROWS * CPR / 64;
-  static_assert(ROWS * CPR % 64 == 0 && INSTR % NWAVES == 0, "whole 1 KiB wave copies, split evenly");
+  static_assert(ROWS * CPR == 4 * 64 * NWAVES, "four 1 KiB wave copies per wave");
+  unsigned o[4];
 #pragma unroll
-  for (int k = 0; k < INSTR / NWAVES; ++k) {
-    const int i = k * NWAVES + wave;
-    const int slot = i * 64 + lane;
+  for (int k = 0; k < 4; ++k) {
+    const int slot = (k * NWAVES + wave) * 64 + lane;
     const int r = slot / CPR, pos = slot % CPR;
     const int c = pos ^ swz<W, M>(r);
-    lds_copy16_untracked(g, (unsigned)(r * ld + c * 8) * 2u, (lds_void*)(tile + i * 512));
+    o[k] = (unsigned)(r * ld + c * 8) * 2u;
   }
+  lds_copy16x4_untracked<NWAVES * 1024>(g, o[0], o[1], o[2], o[3], (lds_void*)(tile + wave * 512));
 }
 
 // Wait until at most N of this wave's vector loads (LDS copies included) are

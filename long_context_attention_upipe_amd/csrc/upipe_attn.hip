@@ -267,6 +267,19 @@ void launch_attn_fwd_bf16(FwdParams<bf16> fp, hipStream_t st) {
   }
 }
 
+// The bf16 dQ kernel: the two-group kernel (256 rows per workgroup) at
+// d = 128, the 4-wave kernel (128 rows) at d = 64. Sets bp.n_qtiles for it.
+template <int D>
+void launch_attn_dq_bf16(BwdParams<bf16> bp, hipStream_t st) {
+  if constexpr (D == 128) {
+    bp.n_qtiles = (bp.S + Bf16Tiles::kDqPpRows - 1) / Bf16Tiles::kDqPpRows;
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_pp_kernel<D>), dim3(bp.n_qtiles * bp.hc), dim3(512), 0, st, bp);
+  } else {
+    bp.n_qtiles = (bp.S + Bf16Tiles::kDqRows - 1) / Bf16Tiles::kDqRows;
+    hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D>), dim3(bp.n_qtiles * bp.hc), dim3(256), 0, st, bp);
+  }
+}
+
 template <typename T, int D>
 int run_fwd(const Problem& pr, const void* q, const void* k, const void* v, void* out, void* out_lo, float* lse,
             char* ws, hipStream_t st) {
@@ -415,7 +428,7 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
     });
     timed(K_BWD_DQ, st, [&] {
       if constexpr (std::is_same<T, bf16>::value)
-        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, bp);
+        launch_attn_dq_bf16<D>(bp, st);
       else
         hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, bp);
     });
@@ -787,7 +800,7 @@ int run_block_bwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
       hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<D>), dim3(n_ktiles * pr.nkv), dim3(256), 0, st, bp);
     });
     timed(K_BWD_DQ, st, [&] {
-      hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<D>), dim3(n_qtiles * pr.hc), dim3(256), 0, st, bp);
+      launch_attn_dq_bf16<D>(bp, st);
     });
     if (int rc = check_launch("attention block backward chunk")) return rc;
 
