@@ -220,6 +220,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdParams<bf16> p
 // reads of the first AHEAD MFMAs, then one MFMA and R reads at a time, then
 // the last AHEAD MFMAs (instruction-scheduler groups; no effect on the
 // results).
+// The same for N pairs of MFMAs whose operands take R LDS reads per pair,
+// AHEAD pairs ahead.
+template <int N, int AHEAD, int R>
+__device__ __forceinline__ void mfma_pair_ds_pipeline() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * AHEAD, 0);
+}
+
 template <int N, int AHEAD, int R = 1>
 __device__ __forceinline__ void mfma_ds_pipeline() {
   __builtin_amdgcn_sched_group_barrier(0x100, R * AHEAD, 0);  // DS reads
@@ -921,6 +934,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
         mma32(s, tile_row_frag<D, kSwzAll>(sQ[cur], col, 2 * ks + half), kf[ks]);
         mma32(dp, tile_row_frag<D, kSwzAll>(sO[cur], col, 2 * ks + half), tile_row_frag<D, kSwzAll>(sV, wave * 32 + col, 2 * ks + half));
       }
+      // fragments read ahead of their MFMAs (three reads per pair)
+      mfma_pair_ds_pipeline<NKS, 2, 3>();
       __builtin_amdgcn_s_setprio(0);
       const bool need_mask = r0 < w_first_max || r0 + BQ - 1 > w_last_min;
       if (need_mask) {
@@ -963,6 +978,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
           mma32(dk[db], tile_tr_frag<D, kSwzAll>(sQ[cur], st * 16, db * 32, lane), dsf);
         }
       }
+      // two transposed reads per MFMA, two MFMAs ahead
+      mfma_ds_pipeline<2 * 2 * NDB, 2, 2>();
       __builtin_amdgcn_s_setprio(0);
     }
     advance(cur_hi, cur_qb);
