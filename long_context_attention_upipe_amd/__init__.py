@@ -94,9 +94,10 @@ def attention_backward(q, k, v, out, dout, lse, out_lo=None, head_chunk=1, causa
     return dq, dk, dv
 
 
-def wait_reporting(what, device=None, interval=10.0, prefix="[upipe]"):
-    """Block until enqueued work is done, printing a line (to stderr) as the
-    library's kernels finish, at most every ``interval`` seconds.
+def wait_reporting(what, device=None, interval=10.0, prefix="[upipe]", log=None):
+    """Block until enqueued work is done, printing a line (to stderr, or
+    through ``log``) as the library's kernels finish, at most every
+    ``interval`` seconds.
 
     Kernels are counted only while profiling is on (``upipe_profile_enable``);
     with it off this is a plain device synchronize. Multi-million-token calls
@@ -111,7 +112,11 @@ def wait_reporting(what, device=None, interval=10.0, prefix="[upipe]"):
         done, total = upipe_profile_completed()
         now = time.perf_counter()
         if done > seen and (done == total or now - last > interval):
-            print(f"{prefix} {what}: {done}/{total} kernels finished", file=sys.stderr, flush=True)
+            line = f"{prefix} {what}: {done}/{total} kernels finished"
+            if log is None:
+                print(line, file=sys.stderr, flush=True)
+            else:
+                log(line)
             seen, last = done, now
         if done == total:
             break

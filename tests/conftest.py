@@ -30,6 +30,9 @@ _keep_freed_heap_memory()
 
 
 def pytest_configure(config):
+    import gpu_util
+
+    gpu_util.PYTEST_CONFIG = config
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: multi-minute GPU case (full-size workloads)")
 
@@ -43,3 +46,4 @@ def pytest_collection_modifyitems(config, items):
         return 1 if it.get_closest_marker("slow") else 0
 
     items.sort(key=rank)
+

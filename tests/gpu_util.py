@@ -4,6 +4,8 @@ compare with the oracle under the stated tolerances."""
 import os
 import time
 
+import sys
+
 import numpy as np
 import torch
 
@@ -117,6 +119,22 @@ def assert_close(name, got, ref, dtype, rel_only=False, grad_scale=1.0, per_item
 PER_ITEM_FACTOR = 4.0
 
 
+PYTEST_CONFIG = None  # set by conftest.pytest_configure
+
+
+def progress(msg):
+    """Print a progress line straight to the terminal, past pytest's output
+    capture, so that a minutes-long GPU case run under -q shows it is
+    advancing (its kernels finishing) while it runs."""
+    capman = PYTEST_CONFIG.pluginmanager.getplugin("capturemanager") if PYTEST_CONFIG else None
+    if capman is None:
+        print(msg, flush=True)
+        return
+    with capman.global_and_fixture_disabled():
+        sys.stdout.write(msg + "\n")
+        sys.stdout.flush()
+
+
 def bit_equal(a, b):
     return torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a.view(torch.int32),
                        b.view(torch.uint8) if b.dtype != torch.float32 else b.view(torch.int32))
@@ -159,7 +177,7 @@ class OracleJobs:
             fut.result()
             now = time.perf_counter()
             if now - last > 20 or n_done == len(futures):
-                print(f"   oracle {label}: {n_done}/{len(futures)} parts, {now - self._t0:.0f}s", flush=True)
+                progress(f"   oracle {label}: {n_done}/{len(futures)} parts, {now - self._t0:.0f}s")
                 last = now
         return [f.result() for f in futures]
 

@@ -21,7 +21,7 @@ import pytest
 import torch
 
 import long_context_attention_upipe_amd as up
-from gpu_util import OracleJobs, assert_close, bit_equal, f64, grad_scale, interleaved_parts, sum64
+from gpu_util import OracleJobs, assert_close, bit_equal, f64, grad_scale, interleaved_parts, progress, sum64
 from long_context_attention_upipe_amd.workloads import WORKLOADS, Workload, make_inputs, sample_rows, tail_keys
 from oracle.attention import backward_cols_dkdv, cols_rows_needed, forward_rows, rows_forward_dq
 
@@ -33,13 +33,13 @@ def _run_chunks(w, q, k, v, do, head_chunks, causal=True):
     after checking that the others are bit-identical to it."""
     results = {}
     for hc in head_chunks:
-        print(f"   {w.name}: head_chunk={hc} causal={causal}", flush=True)
+        progress(f"   {w.name}: head_chunk={hc} causal={causal}")
         ws = up.workspace(w.S, w.Hq, w.Hkv, w.d, hc, q.dtype, q.device, "both")
         up.upipe_profile_reset()
         up.upipe_profile_enable(True)
         out, lse, out_lo = up.attention_forward(q, k, v, head_chunk=hc, causal=causal, ws=ws)
         dq, dk, dv = up.attention_backward(q, k, v, out, do, lse, out_lo, head_chunk=hc, causal=causal, ws=ws)
-        up.wait_reporting(f"head_chunk={hc}", q.device, prefix="  ")
+        up.wait_reporting(f"head_chunk={hc}", q.device, prefix="  ", log=progress)
         up.upipe_profile_enable(False)
         up.upipe_profile_reset()
         del ws, out_lo
@@ -55,8 +55,8 @@ def _run_chunks(w, q, k, v, do, head_chunks, causal=True):
 def _check(w, head_chunks, n_rows, n_keys, key_window, causal=True):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    print(f"\n  case {w.name} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} head_chunks={head_chunks} causal={causal} "
-          f"rows={n_rows} keys={n_keys if causal else 0}", flush=True)
+    progress(f"\n  case {w.name} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} head_chunks={head_chunks} causal={causal} "
+             f"rows={n_rows} keys={n_keys if causal else 0}")
     dev = torch.device("cuda:0")
     q, k, v, do = make_inputs(w, device=dev)
     rows = sample_rows(w.S, n_rows, seed=w.seed + 7)
@@ -176,8 +176,7 @@ def test_llama8b_share_128k_full_tensors_every_head_chunk():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     w = WORKLOADS["llama8b_share_s128k"]
-    print(f"\n  case {w.name} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} head_chunks={w.head_chunks} full tensors",
-          flush=True)
+    progress(f"\n  case {w.name} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} head_chunks={w.head_chunks} full tensors")
     dev = torch.device("cuda:0")
     q, k, v, do = make_inputs(w, device=dev)
     qc, kc, vc, doc = f64(q), f64(k), f64(v), f64(do)
