@@ -915,6 +915,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(BwdParams<bf
     if (step + 1 < n_steps) {
       issue(next_hi, next_qb, cur ^ 1);
       advance(next_hi, next_qb);
+      // Every fourth step the copy just issued is waited for at once. A
+      // workgroup that has run ahead of the others sharing its Q/dO blocks
+      // misses in L2 and pays that latency here, which holds it back to
+      // them; without this they drift apart over long walks (several heads
+      // per chunk) and fetch far more from beyond L2.
+      if ((step & 3) == 0) wait_vm();
     }
     const int r0 = cur_qb * BQ;
     const bool active = (wkey0 < S) && r0 + BQ - 1 >= w_first_min && r0 <= w_last_max;
