@@ -218,6 +218,44 @@ int upipe_attn_bwd_docs(const void* q, const void* k, const void* v,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Fused deterministic backward ("Road to 5 Million Tokens" talk summary,
+ * Chapters: the activation-checkpointing chapter -- the backward rebuilds what
+ * the forward did not keep; this call rebuilds the scores once per (row
+ * block, key tile) pair instead of twice). The same inputs, outputs and
+ * formulas as upipe_attn_bwd, from one kv-major kernel that also forms dq:
+ * five products per pair instead of seven. dq is summed in a fixed order (per
+ * XCD of the device: key tiles in ascending order, each adding after the one
+ * before it; then the XCDs' partial sums in ascending order), so repeated
+ * calls, and calls with any head_chunk, give bit-identical dq, dk, dv. The
+ * values differ from upipe_attn_bwd's by rounding only (another summation
+ * order).
+ * Limits: bf16 (dtype implied), d = 128, (S + 32) * 512 < 2^32; no document
+ *   masks. Other shapes fail with UPIPE_EUNSUPPORTED before anything is
+ *   enqueued.
+ * max_polls: the longest any wait for another workgroup may poll (0 selects
+ *   2^20, seconds). If a wait runs out -- it cannot while the device runs the
+ *   call's kernels, but the limit guarantees that every kernel ends -- every
+ *   dq value of the chunk is written as NaN instead; dk, dv are then
+ *   unspecified. Nothing else changes.
+ * Workspace: upipe_attn_bwd_fused_workspace_bytes(); beyond the
+ *   upipe_attn_bwd pool it holds eight fp32 dq partial sums of head_chunk
+ *   heads (8 * head_chunk * S * d * 4 bytes: 4 GiB per head at S = 1,048,576).
+ *   Calls that share a workspace must be serialized (stream order is enough).
+ * Returns 0 when everything was enqueued on `stream`; the result of a wait
+ * that gave up shows only in dq, as above.
+ */
+size_t upipe_attn_bwd_fused_workspace_bytes(int64_t S, int Hq, int Hkv, int d,
+                                            int head_chunk);
+
+int upipe_attn_bwd_fused(const void* q, const void* k, const void* v,
+                         const void* out, const void* out_lo, const void* dout,
+                         const float* lse,
+                         void* dq, void* dk, void* dv,
+                         int64_t S, int Hq, int Hkv, int d, int head_chunk,
+                         int causal, int max_polls,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * bf16 GEMM with fp32 accumulation on the MFMA units (the projections around
  * the chunked attention use it; exported so it can be checked on its own):
  *   C[M, N] = A[M, K] B[K, N]   (accumulate != 0, fp32 C only: C += A B)

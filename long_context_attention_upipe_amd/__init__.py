@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     upipe_attn_block_fwd_workspace_bytes,
     upipe_attn_bwd,
     upipe_attn_bwd_docs,
+    upipe_attn_bwd_fused,
+    upipe_attn_bwd_fused_workspace_bytes,
     upipe_attn_bwd_workspace_bytes,
     upipe_attn_fwd,
     upipe_attn_fwd_docs,
@@ -91,6 +93,21 @@ def attention_backward(q, k, v, out, dout, lse, out_lo=None, head_chunk=1, causa
     else:
         upipe_attn_bwd_docs(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, doc_offsets, ws,
                             stream)
+    return dq, dk, dv
+
+
+def attention_backward_fused(q, k, v, out, dout, lse, out_lo=None, head_chunk=1, causal=True, ws=None,
+                             stream=None, max_polls=0):
+    """dq, dk, dv from the fused deterministic backward (bf16, d = 128)."""
+    import torch
+
+    S, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if ws is None:
+        ws = torch.empty(upipe_attn_bwd_fused_workspace_bytes(S, Hq, Hkv, d, head_chunk), dtype=torch.uint8,
+                         device=q.device)
+    upipe_attn_bwd_fused(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, ws, max_polls, stream)
     return dq, dk, dv
 
 

@@ -55,6 +55,11 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz,
                                  vp]
     L.upipe_attn_bwd.restype = i32
+    L.upipe_attn_bwd_fused_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+    L.upipe_attn_bwd_fused_workspace_bytes.restype = sz
+    L.upipe_attn_bwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp,
+                                       sz, vp]
+    L.upipe_attn_bwd_fused.restype = i32
     L.upipe_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     L.upipe_attn_fwd_noalloc.restype = i32
     L.upipe_gemm_bf16.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, i32, i32, i32,
@@ -134,6 +139,14 @@ def upipe_attn_bwd_workspace_bytes(S, Hq, Hkv, d, head_chunk, dtype) -> int:
     n = lib().upipe_attn_bwd_workspace_bytes(S, Hq, Hkv, d, head_chunk, dtype)
     if n == 0:
         raise UpipeError(-1, upipe_last_error())
+    return n
+
+
+def upipe_attn_bwd_fused_workspace_bytes(S, Hq, Hkv, d, head_chunk) -> int:
+    """Bytes of the fused backward's pool (bf16, d = 128)."""
+    n = lib().upipe_attn_bwd_fused_workspace_bytes(S, Hq, Hkv, d, head_chunk)
+    if n == 0:
+        raise UpipeError(-2, upipe_last_error())
     return n
 
 
@@ -256,6 +269,28 @@ def upipe_attn_bwd(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, caus
                                     _ptr(dq), _ptr(dk), _ptr(dv), S, Hq, Hkv, d,
                                     int(head_chunk), int(causal), dtype_code(q.dtype),
                                     _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+
+
+def upipe_attn_bwd_fused(q, k, v, out, out_lo, dout, lse, dq, dk, dv, head_chunk, causal, workspace,
+                         max_polls=0, stream=None) -> None:
+    """Enqueue the fused deterministic backward (bf16, d = 128) on ``stream``.
+    ``max_polls`` bounds every wait for another workgroup (0: the library's
+    default); a wait that runs out leaves dq all NaN."""
+    S, Hq, Hkv, d = _shape(q, k)
+    if q.dtype != torch.bfloat16:
+        raise UpipeError(-2, f"the fused backward supports bf16 only (got {q.dtype})")
+    _require((q, k, v, out, dout, dq, dk, dv) + ((out_lo,) if out_lo is not None else ()), q.dtype)
+    _require((lse,), torch.float32)
+    _require((workspace,), torch.uint8)
+    qs, ks = (S, Hq, d), (S, Hkv, d)
+    _require_shapes(q, [("k", k, ks), ("v", v, ks), ("out", out, qs), ("out_lo", out_lo, qs), ("dout", dout, qs),
+                        ("lse", lse, (Hq, S)), ("dq", dq, qs), ("dk", dk, ks), ("dv", dv, ks),
+                        ("workspace", workspace, (workspace.numel(),))])
+    with torch.cuda.device(q.device):
+        _check(lib().upipe_attn_bwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(out_lo), _ptr(dout),
+                                          _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), S, Hq, Hkv, d,
+                                          int(head_chunk), int(causal), int(max_polls),
+                                          _ptr(workspace), workspace.numel(), _stream_handle(stream)))
 
 
 def _require_docs(q, doc_offsets, check_values=True) -> int:

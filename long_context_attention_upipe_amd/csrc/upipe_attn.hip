@@ -25,6 +25,7 @@
 
 #include "attn_bf16.hpp"
 #include "attn_bwd.hpp"
+#include "attn_bwd_fused.hpp"
 #include "attn_fwd.hpp"
 #include "copy_kernels.hpp"
 #include "gemm_bf16.hpp"
@@ -178,9 +179,13 @@ struct Tiles {
 // ---------------------------------------------------------------------------
 // Optional per-kernel timing with HIP events on the launch stream.
 // ---------------------------------------------------------------------------
-enum KernelId { K_PACK = 0, K_UNPACK, K_FWD, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_GEMM, K_CE_ROWS, K_SWIGLU, K_COUNT };
+enum KernelId {
+  K_PACK = 0, K_UNPACK, K_FWD, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ, K_GEMM, K_CE_ROWS, K_SWIGLU, K_BWD_FUSED, K_DQ_REDUCE,
+  K_COUNT
+};
 const char* const kKernelNames[K_COUNT] = {"pack_heads", "unpack_heads", "attn_fwd", "bwd_pre", "attn_bwd_dkdv",
-                                           "attn_bwd_dq", "gemm_bf16", "ce_rows", "swiglu"};
+                                           "attn_bwd_dq", "gemm_bf16", "ce_rows", "swiglu", "attn_bwd_fused",
+                                           "fused_dq_reduce"};
 struct Profiler {
   std::atomic<bool> on{false};
   struct Rec {
@@ -437,6 +442,181 @@ int run_bwd(const Problem& pr, const void* q, const void* k, const void* v, cons
                          pr.Hq, c.q_head0, pr.hc, vpr);
     });
     if (int rc = check_launch("backward chunk")) return rc;
+  }
+  return UPIPE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The fused deterministic backward (attn_bwd_fused.hpp): bf16, d = 128, no
+// document masks. Pool: the two-kernel backward's buffers without its packed
+// dQ, plus one fp32 dQ partial per XCD and the queue/progress words.
+// ---------------------------------------------------------------------------
+constexpr int kMaxXcd = 8;
+constexpr int kDefaultMaxPolls = 1 << 20;
+
+struct FusedPool {
+  size_t q, dout, k, v, neg_d, lse2, dk_acc, dv_acc, partial, sync, total;
+  size_t sync_ints;  // tickets [kMaxXcd], error [1], progress [n_ktiles][nkv][4]
+  bool has_acc;
+};
+FusedPool fused_pool(const Problem& pr) {
+  const size_t U = (size_t)pr.S * pr.d * pr.es;
+  const int64_t n_ktiles = (pr.S + Bf16Tiles::kDkvKeys - 1) / Bf16Tiles::kDkvKeys;
+  FusedPool p;
+  size_t off = 0;
+  p.q = off; off += align_up(pr.hc * U);
+  p.dout = off; off += align_up(pr.hc * U);
+  p.k = off; off += align_up(pr.nkv * U);
+  p.v = off; off += align_up(pr.nkv * U);
+  p.neg_d = off; off += align_up((size_t)pr.hc * pr.S * 4);
+  p.lse2 = off; off += align_up((size_t)pr.hc * pr.S * 4);
+  p.has_acc = pr.hc < pr.G;
+  const size_t A = (size_t)pr.S * pr.d * 4;
+  p.dk_acc = off; off += p.has_acc ? align_up(A) : 0;
+  p.dv_acc = off; off += p.has_acc ? align_up(A) : 0;
+  p.partial = off; off += align_up((size_t)kMaxXcd * pr.hc * A);
+  p.sync_ints = kMaxXcd + 1 + (size_t)n_ktiles * pr.nkv * 4;
+  p.sync = off; off += align_up(p.sync_ints * 4);
+  p.total = off;
+  return p;
+}
+
+// The fused path's limits on top of validate(): bf16 heads of 128, and the
+// per-XCD partial of one head addressed with 32-bit byte offsets.
+int validate_fused(const Problem& pr) {
+  if (pr.dtype != UPIPE_BF16) return fail(UPIPE_EUNSUPPORTED, "the fused backward supports bf16 only");
+  if (pr.d != 128) return fail(UPIPE_EUNSUPPORTED, "the fused backward supports d = 128 only (got %d)", pr.d);
+  if ((uint64_t)(pr.S + Bf16Tiles::kDkvRows) * 128 * 4 > 0xFFFFFFFFull)
+    return fail(UPIPE_EUNSUPPORTED, "the fused backward needs (S + 32) * 512 < 2^32 (S = %lld)", (long long)pr.S);
+  return UPIPE_OK;
+}
+
+// XCD count and resident-workgroup capacity of the current device, looked up
+// once per device.
+struct DeviceShape {
+  int nx = 0, cus = 0;
+};
+std::mutex g_shape_mu;
+std::vector<DeviceShape> g_shapes;
+
+int device_shape(DeviceShape* out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(UPIPE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_shape_mu);
+  if ((int)g_shapes.size() <= dev) g_shapes.resize(dev + 1);
+  DeviceShape& d = g_shapes[dev];
+  if (!d.nx) {
+    int nx = 0, cus = 0;
+    e = hipDeviceGetAttribute(&nx, hipDeviceAttributeNumberOfXccs, dev);
+    if (e != hipSuccess) return fail(UPIPE_EHIP, "XCD count of device %d: %s", dev, hipGetErrorString(e));
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(UPIPE_EHIP, "CU count of device %d: %s", dev, hipGetErrorString(e));
+    if (nx < 1 || nx > kMaxXcd) return fail(UPIPE_EUNSUPPORTED, "device %d reports %d XCDs (1..%d)", dev, nx, kMaxXcd);
+    d.nx = nx;
+    d.cus = std::max(cus, nx);
+  }
+  *out = d;
+  return UPIPE_OK;
+}
+
+template <int D>
+int run_bwd_fused(const Problem& pr, const void* q, const void* k, const void* v, const void* out,
+                  const void* out_lo, const void* dout, const float* lse, void* dq, void* dk, void* dv, char* ws,
+                  int max_polls, hipStream_t st) {
+  static_assert(D == 128, "the fused kernel is written for d = 128");
+  DeviceShape dsh;
+  if (int rc = device_shape(&dsh)) return rc;
+  const FusedPool pool = fused_pool(pr);
+  const int S = (int)pr.S;
+  const int vpr = D * 2 / 16;
+  bf16* Qc = reinterpret_cast<bf16*>(ws + pool.q);
+  bf16* dOc = reinterpret_cast<bf16*>(ws + pool.dout);
+  bf16* Kc = reinterpret_cast<bf16*>(ws + pool.k);
+  bf16* Vc = reinterpret_cast<bf16*>(ws + pool.v);
+  float* nDc = reinterpret_cast<float*>(ws + pool.neg_d);
+  float* L2c = reinterpret_cast<float*>(ws + pool.lse2);
+  float* dKa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dk_acc) : nullptr;
+  float* dVa = pool.has_acc ? reinterpret_cast<float*>(ws + pool.dv_acc) : nullptr;
+  int* sync = reinterpret_cast<int*>(ws + pool.sync);
+  const int n_ktiles = (S + Bf16Tiles::kDkvKeys - 1) / Bf16Tiles::kDkvKeys;
+  const float scale = 1.0f / std::sqrt((float)D);
+  constexpr int kRowsPerPreBlock = 256 / (D * 2 / 16);
+  // Resident capacity (two workgroups per CU), at least one workgroup per
+  // XCD; workgroups past the tiles of their XCD's queue leave at once.
+  const int n_tiles = n_ktiles * pr.nkv;
+  const unsigned grid = (unsigned)std::max(std::min(2 * dsh.cus, n_tiles), dsh.nx);
+  for (const Chunk& c : plan(pr)) {
+    if (c.load_kv) {
+      const size_t nv = (size_t)S * c.n_kv * vpr;
+      timed(K_PACK, st, [&] {
+        hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)k, (uint4*)Kc, S,
+                           pr.Hkv, c.kv_head0, c.n_kv, vpr);
+      });
+      timed(K_PACK, st, [&] {
+        hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nv)), dim3(256), 0, st, (const uint4*)v, (uint4*)Vc, S,
+                           pr.Hkv, c.kv_head0, c.n_kv, vpr);
+      });
+    }
+    const size_t nq = (size_t)S * pr.hc * vpr;
+    timed(K_PACK, st, [&] {
+      hipLaunchKernelGGL(pack_heads_kernel, dim3(copy_grid(nq)), dim3(256), 0, st, (const uint4*)q, (uint4*)Qc, S,
+                         pr.Hq, c.q_head0, pr.hc, vpr);
+    });
+    const size_t rows = (size_t)S * pr.hc;
+    const unsigned pre_grid =
+        (unsigned)std::min<size_t>((rows + kRowsPerPreBlock - 1) / kRowsPerPreBlock, 256 * 32);
+    timed(K_BWD_PRE, st, [&] {
+      const int64_t tok = (int64_t)pr.Hq * D, h0 = (int64_t)c.q_head0 * D;
+      const RowsView<bf16> o_v{reinterpret_cast<const bf16*>(out) + h0, tok, D};
+      const RowsView<bf16> lo_v{out_lo ? reinterpret_cast<const bf16*>(out_lo) + h0 : nullptr, tok, D};
+      const RowsView<bf16> do_v{reinterpret_cast<const bf16*>(dout) + h0, tok, D};
+      hipLaunchKernelGGL((bwd_pre_kernel<bf16, D>), dim3(pre_grid), dim3(256), 0, st, o_v, lo_v, do_v,
+                         lse + (size_t)c.q_head0 * S, dOc, nDc, L2c, S, pr.hc);
+    });
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(copy_grid(pool.sync_ints)), dim3(256), 0, st, sync, pool.sync_ints);
+
+    BwdParams<bf16> bp = {};
+    bp.q = Qc;
+    bp.k = Kc;
+    bp.v = Vc;
+    bp.dout = dOc;
+    bp.lse = lse + (size_t)c.q_head0 * S;
+    bp.negD = nDc;
+    bp.lse2 = L2c;
+    bp.dq = nullptr;
+    bp.dk_acc = dKa;
+    bp.dv_acc = dVa;
+    bp.dk_out = reinterpret_cast<bf16*>(dk) + (size_t)c.kv_head0 * D;
+    bp.dv_out = reinterpret_cast<bf16*>(dv) + (size_t)c.kv_head0 * D;
+    bp.Hkv_total = pr.Hkv;
+    bp.S = S;
+    bp.hc = pr.hc;
+    bp.heads_per_kv = pr.heads_per_kv;
+    bp.nkv = pr.nkv;
+    bp.n_ktiles = n_ktiles;
+    bp.causal = pr.causal;
+    bp.acc_load = !c.first_for_kv;
+    bp.finalize = c.last_for_kv;
+    bp.scale = scale;
+    bp.scale_log2 = scale * kLog2e;
+    FusedSync fs;
+    fs.partial = reinterpret_cast<float*>(ws + pool.partial);
+    fs.tickets = sync;
+    fs.error = sync + kMaxXcd;
+    fs.progress = sync + kMaxXcd + 1;
+    fs.nx = dsh.nx;
+    fs.max_polls = max_polls;
+    timed(K_BWD_FUSED, st, [&] {
+      hipLaunchKernelGGL((attn_bwd_fused_bf16_kernel<D>), dim3(grid), dim3(256), 0, st, bp, fs);
+    });
+    timed(K_DQ_REDUCE, st, [&] {
+      const size_t n4 = (size_t)pr.hc * S * D / 4;
+      hipLaunchKernelGGL(fused_dq_reduce_kernel, dim3(copy_grid(n4)), dim3(256), 0, st, fs.partial, fs.tickets,
+                         fs.error, reinterpret_cast<bf16*>(dq) + (size_t)c.q_head0 * D, (int64_t)pr.Hq * D, S, pr.hc,
+                         dsh.nx, n_ktiles, pr.nkv, pr.causal, scale);
+    });
+    if (int rc = check_launch("fused backward chunk")) return rc;
   }
   return UPIPE_OK;
 }
@@ -1051,6 +1231,14 @@ size_t upipe_attn_workspace_bytes(int64_t S, int Hq, int Hkv, int d, int head_ch
   return std::max(fwd_pool(pr).total, bwd_pool(pr).total);
 }
 
+size_t upipe_attn_bwd_fused_workspace_bytes(int64_t S, int Hq, int Hkv, int d, int head_chunk) {
+  Problem pr;
+  if (validate(S, Hq, Hkv, d, head_chunk, 1, UPIPE_BF16, &pr) != UPIPE_OK) return 0;
+  if (validate_fused(pr) != UPIPE_OK) return 0;
+  g_error.clear();
+  return fused_pool(pr).total;
+}
+
 int upipe_attn_pick_head_chunk(int64_t S, int Hq, int Hkv, int d, int dtype, size_t budget_bytes) {
   Problem pr;
   if (int rc = validate(S, Hq, Hkv, d, 1, 1, dtype, &pr)) return rc;
@@ -1197,6 +1385,30 @@ int upipe_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                    void* stream) {
   return bwd_entry(q, k, v, out, out_lo, dout, lse, dq, dk, dv, S, Hq, Hkv, d, head_chunk, causal, nullptr, 0,
                    dtype, workspace, workspace_bytes, stream);
+}
+
+int upipe_attn_bwd_fused(const void* q, const void* k, const void* v, const void* out, const void* out_lo,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int64_t S, int Hq,
+                         int Hkv, int d, int head_chunk, int causal, int max_polls, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Problem pr;
+  if (int rc = validate(S, Hq, Hkv, d, head_chunk, causal, UPIPE_BF16, &pr)) return rc;
+  if (int rc = validate_fused(pr)) return rc;
+  const void* ptrs[] = {q, k, v, out, dout, lse, dq, dk, dv, workspace};
+  const char* names[] = {"q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv", "workspace"};
+  for (int i = 0; i < 10; ++i) {
+    if (!ptrs[i]) return fail(UPIPE_EINVAL, "%s is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(UPIPE_EINVAL, "%s is not 16-byte aligned", names[i]);
+  }
+  if (out_lo && !aligned16(out_lo)) return fail(UPIPE_EINVAL, "out_lo is not 16-byte aligned");
+  if (max_polls < 0) return fail(UPIPE_EINVAL, "max_polls must be >= 0 (got %d)", max_polls);
+  const size_t need = fused_pool(pr).total;
+  if (workspace_bytes < need)
+    return fail(UPIPE_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  g_error.clear();
+  (void)hipGetLastError();
+  return run_bwd_fused<128>(pr, q, k, v, out, out_lo, dout, lse, dq, dk, dv, reinterpret_cast<char*>(workspace),
+                            max_polls ? max_polls : kDefaultMaxPolls, reinterpret_cast<hipStream_t>(stream));
 }
 
 int upipe_attn_bwd_docs(const void* q, const void* k, const void* v, const void* out, const void* out_lo,

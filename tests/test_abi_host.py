@@ -379,3 +379,33 @@ def test_tiled_mlp_host_checks():
     assert lib.upipe_mlp_tiled_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1000, 128, 256, 128, FAKE,
                                    1 << 40, None) == -1
     assert "dx is NULL" in L.upipe_last_error()
+
+
+def test_fused_backward_host_checks():
+    lib = L.lib()
+    S = 1 << 20
+    n1 = L.upipe_attn_bwd_fused_workspace_bytes(S, 4, 1, 128, 1)
+    n4 = L.upipe_attn_bwd_fused_workspace_bytes(S, 4, 1, 128, 4)
+    assert n1 < n4
+    # the two-kernel pool without its packed dq, plus eight fp32 dq partials of the chunk's heads
+    two_kernel = L.upipe_attn_bwd_workspace_bytes(S, 4, 1, 128, 1, L.UPIPE_BF16)
+    assert n1 >= two_kernel - S * 128 * 2 + 8 * S * 128 * 4
+    assert lib.upipe_attn_bwd_fused_workspace_bytes(1000, 4, 1, 64, 1) == 0
+    assert "d = 128" in L.upipe_last_error()
+    assert lib.upipe_attn_bwd_fused_workspace_bytes(8388576, 1, 1, 128, 1) == 0
+    assert "2^32" in L.upipe_last_error()
+    assert lib.upipe_attn_bwd_fused_workspace_bytes(8388575, 1, 1, 128, 1) > 0
+
+    def call(**kw):
+        a = dict(dq=FAKE, S=1000, Hq=4, Hkv=1, d=128, hc=1, causal=1, polls=0, ws=1 << 40)
+        a.update(kw)
+        return lib.upipe_attn_bwd_fused(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, a["dq"], FAKE, FAKE, a["S"],
+                                        a["Hq"], a["Hkv"], a["d"], a["hc"], a["causal"], a["polls"], FAKE, a["ws"],
+                                        None)
+
+    assert call(d=64) == -2 and "d = 128" in L.upipe_last_error()
+    assert call(dq=None) == -1 and "dq is NULL" in L.upipe_last_error()
+    assert call(polls=-1) == -1 and "max_polls" in L.upipe_last_error()
+    assert call(ws=16) == -3 and "workspace too small" in L.upipe_last_error()
+    assert call(hc=3) == -1 and "must divide Hq" in L.upipe_last_error()
+    assert call(causal=2) == -1

@@ -21,24 +21,30 @@ import pytest
 import torch
 
 import long_context_attention_upipe_amd as up
-from gpu_util import OracleJobs, assert_close, bit_equal, f64, grad_scale, interleaved_parts, progress, sum64
+from gpu_util import TOL, OracleJobs, assert_close, bit_equal, f64, grad_scale, interleaved_parts, progress, sum64
 from long_context_attention_upipe_amd.workloads import WORKLOADS, Workload, make_inputs, sample_rows, tail_keys
 from oracle.attention import backward_cols_dkdv, cols_rows_needed, forward_rows, rows_forward_dq
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def _run_chunks(w, q, k, v, do, head_chunks, causal=True):
-    """Forward + backward at every head_chunk; returns the first one's outputs
-    after checking that the others are bit-identical to it."""
+def _run_chunks(w, q, k, v, do, head_chunks, causal=True, fused=False):
+    """Forward + backward (the two-kernel one, or the fused one) at every
+    head_chunk; returns the first one's outputs after checking that the others
+    are bit-identical to it."""
     results = {}
     for hc in head_chunks:
-        progress(f"   {w.name}: head_chunk={hc} causal={causal}")
-        ws = up.workspace(w.S, w.Hq, w.Hkv, w.d, hc, q.dtype, q.device, "both")
+        progress(f"   {w.name}: head_chunk={hc} causal={causal} fused={fused}")
+        ws = up.workspace(w.S, w.Hq, w.Hkv, w.d, hc, q.dtype, q.device, "fwd" if fused else "both")
         up.upipe_profile_reset()
         up.upipe_profile_enable(True)
         out, lse, out_lo = up.attention_forward(q, k, v, head_chunk=hc, causal=causal, ws=ws)
-        dq, dk, dv = up.attention_backward(q, k, v, out, do, lse, out_lo, head_chunk=hc, causal=causal, ws=ws)
+        if fused:
+            del ws
+            dq, dk, dv = up.attention_backward_fused(q, k, v, out, do, lse, out_lo, head_chunk=hc, causal=causal)
+            ws = None
+        else:
+            dq, dk, dv = up.attention_backward(q, k, v, out, do, lse, out_lo, head_chunk=hc, causal=causal, ws=ws)
         up.wait_reporting(f"head_chunk={hc}", q.device, prefix="  ", log=progress)
         up.upipe_profile_enable(False)
         up.upipe_profile_reset()
@@ -52,11 +58,11 @@ def _run_chunks(w, q, k, v, do, head_chunks, causal=True):
     return results[head_chunks[0]]
 
 
-def _check(w, head_chunks, n_rows, n_keys, key_window, causal=True):
+def _check(w, head_chunks, n_rows, n_keys, key_window, causal=True, fused=False):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     progress(f"\n  case {w.name} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d} head_chunks={head_chunks} causal={causal} "
-             f"rows={n_rows} keys={n_keys if causal else 0}")
+             f"rows={n_rows} keys={n_keys if causal else 0} fused={fused}")
     dev = torch.device("cuda:0")
     q, k, v, do = make_inputs(w, device=dev)
     rows = sample_rows(w.S, n_rows, seed=w.seed + 7)
@@ -86,7 +92,7 @@ def _check(w, head_chunks, n_rows, n_keys, key_window, causal=True):
             do32 = np.zeros(tuple(do.shape), dtype=np.float32)
             q32[first:], do32[first:] = q[first:].float().cpu().numpy(), do[first:].float().cpu().numpy()
 
-        r = _run_chunks(w, q, k, v, do, head_chunks, causal)
+        r = _run_chunks(w, q, k, v, do, head_chunks, causal, fused)
 
         gs = grad_scale(w)
         o_ref, l_ref, dq_ref = np.empty_like(qr), np.empty((w.Hq, len(rows))), np.empty_like(qr)
@@ -112,6 +118,7 @@ def _check(w, head_chunks, n_rows, n_keys, key_window, causal=True):
         assert np.all(np.abs(dk_sum[g]) <= 1e-2 * dk_abs[g] + 1e-4)
         ref = sum64(do[:, g * G:(g + 1) * G, :], (0, 1))
         assert_close("dvsum", dv_sum[g], ref, w.dtype)
+    return r
 
 
 def test_llama8b_share_128k_sampled_4096_rows():
@@ -203,3 +210,27 @@ def test_llama8b_share_128k_full_tensors_every_head_chunk():
     assert_close("dq", f64(r["dq"]), dq_ref, w.dtype, grad_scale=gs, per_item=True)
     assert_close("dk", f64(r["dk"]), dk_ref, w.dtype, grad_scale=gs, per_item=True)
     assert_close("dv", f64(r["dv"]), dv_ref, w.dtype, grad_scale=gs, per_item=True)
+
+
+def test_llama8b_share_1m_fused_backward_sampled_4096_rows():
+    """The fused deterministic backward at the bench workload (1,048,576
+    tokens, head_chunk 1 and 4): sampled dQ rows and tail keys against the
+    oracle, bit-identical across head_chunk, and every element within the
+    bf16 tolerance of the two-kernel backward's."""
+    w = WORKLOADS["llama8b_share_s1m"]
+    r = _check(w, (1, 4), 4096, 128, 512, fused=True)
+    progress("   every element against the two-kernel backward")
+    q, k, v, do = make_inputs(w, device=torch.device("cuda:0"))
+    ref = _run_chunks(w, q, k, v, do, (1,))
+    gs = grad_scale(w)
+    max_abs_tol, rel_tol = TOL[w.dtype]
+    for name in ("dq", "dk", "dv"):
+        # on the device, in float32 (both sides are bf16): the same bounds as
+        # against the oracle, at unit dO scale
+        a, b = r[name].float() * gs, ref[name].float() * gs
+        err = (a - b).abs()
+        worst = float((err / b.abs().clamp_min(1.0)).max())
+        rel = float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
+        progress(f"   {name}: max |err| / max(|ref|, 1) = {worst:.3e}, relative Frobenius {rel:.3e}")
+        assert torch.isfinite(a).all()
+        assert worst <= max_abs_tol and rel <= rel_tol, name
