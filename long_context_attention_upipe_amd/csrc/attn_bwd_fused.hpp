@@ -87,6 +87,17 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
+// A progress word read through the scalar unit with the scalar cache
+// bypassed, so it comes from the XCD's L2, where its writer (a workgroup of
+// the same XCD, with an ordinary store) put it. A vector load would also have to wait for this wave's
+// global->LDS copies in flight (they share one counter); this wait counts LDS
+// and scalar operations only. The address must be the same in every lane.
+__device__ __forceinline__ int poll_word(const int* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
 // Workgroup barrier after this wave's LDS accesses have completed; outstanding
 // global memory operations are left in flight (the callers wait for the ones
 // they need by count).
@@ -207,7 +218,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_fused_bf16_kernel(BwdParams<b
     wait_vm();
     __syncthreads();
     int done_code = -1;  // step code of the last step whose additions were issued
-    int seen = 0;        // last value read from the previous tile's progress word
     for (int step = 0; step < n_steps; ++step) {
       const int cur = step & 1;
       const int lane = opaque(tid & 63);
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_fused_bf16_kernel(BwdParams<b
       if (done_code >= 0) {
         wait_vm_leave_n(in_flight);
         asm volatile("" ::: "memory");
-        if (lane == 0) __hip_atomic_store(mine, done_code + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(mine, done_code + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       bf16x8 pf[2], dsf[2];
       if (active) {
@@ -292,27 +302,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_fused_bf16_kernel(BwdParams<b
       const unsigned poff = (unsigned)((r0 + col) * D + wave * 32 + half * 4) * 4u;
       floatx16 dq = floatx16{};
       if (pred) {
-        // Wait for the previous tile's additions to these rows: usually the
-        // progress word read during the last step already shows them; else
-        // poll it. Then start from the partial's current rows (the loads fly
-        // during dV, dK).
-        if (seen <= code) {
-          int polls = 0;
-          for (;;) {
-            seen = __hip_atomic_load(pred, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (seen > code) break;
-            if (__hip_atomic_load(fs.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
-                ++polls >= fs.max_polls) {
-              if (lane == 0) __hip_atomic_store(fs.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
+        // Wait for the previous tile's additions to these rows, then start
+        // from the partial's current rows (the loads fly during dV, dK).
+        int polls = 0;
+        while (poll_word(pred) <= code) {
+          if (__hip_atomic_load(fs.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
+              ++polls >= fs.max_polls) {
+            if (lane == 0) __hip_atomic_store(fs.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
           }
+          __builtin_amdgcn_s_sleep(1);
         }
-        asm volatile("" ::: "memory");
-        // The word again, for the next step: it completes with the partial
-        // loads below, which the dQ products wait for anyway.
-        seen = __hip_atomic_load(pred, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int jg = 0; jg < 4; ++jg) {
           const floatx4 v = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(part, poff + jg * 32, 0, 1));
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_fused_bf16_kernel(BwdParams<b
     wait_vm();
     asm volatile("" ::: "memory");
     if (lane == 0 && done_code >= 0)
-      __hip_atomic_store(mine, done_code + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mine, done_code + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 
     if (key_ok) {
       if (p.finalize) {
