@@ -20,6 +20,10 @@ After the timed headline run, every other head_chunk of the workload runs
 trade-off: TFLOP/s and peak HBM per head_chunk (`head_chunk_sweep`). One more
 step at the headline head_chunk runs without out_lo (the forward's stored
 rounding residual of out) to report peak HBM when D comes from out alone.
+Then one call of the fused deterministic backward (upipe_attn_bwd_fused) on
+the same workload (`fused_backward`: time, TFLOP/s, its speed against the
+two-kernel backward timed above, pool and peak HBM), and the attention block,
+loss and MLP legs (`block_fwd`, `tiled_loss`, `tiled_mlp`).
 """
 
 from __future__ import annotations
@@ -420,6 +424,54 @@ def mlp_leg(dev, S=131072, Dm=4096, F=14336, tile=4096):
     return res
 
 
+def fused_leg(w, hc, dev, two_kernel_bwd_ms):
+    """The fused deterministic backward (upipe_attn_bwd_fused) on the headline
+    workload: the same inputs, forward and head_chunk, one timed backward call
+    (HIP events on the launch stream), its kernels' averages, pool and peak HBM."""
+    import torch
+
+    import long_context_attention_upipe_amd as up
+    from long_context_attention_upipe_amd.workloads import make_inputs
+
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    q, k, v, do = make_inputs(w, device=dev)
+    out, lse, out_lo = up.attention_forward(q, k, v, head_chunk=hc, causal=w.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = up.upipe_attn_bwd_fused_workspace_bytes(w.S, w.Hq, w.Hkv, w.d, hc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    up.upipe_profile_reset()
+    up.upipe_profile_enable(True)
+    e0.record(stream)
+    up.upipe_attn_bwd_fused(q, k, v, out, out_lo, do, lse, dq, dk, dv, hc, w.causal, ws, 0, stream)
+    e1.record(stream)
+    up.wait_reporting("fused backward", dev, prefix="[bench]")
+    up.upipe_profile_enable(False)
+    prof = up.upipe_profile_read()
+    up.upipe_profile_reset()
+    ms = e0.elapsed_time(e1)
+    P = pairs(w.S, w.causal)
+    kernels = {n: {"launches": c, "avg_ms": round(t / max(1, c), 3)} for n, (c, t) in prof.items()
+               if n in ("attn_bwd_fused", "fused_dq_reduce")}
+    res = {"head_chunk": hc, "steps": 1, "bwd_ms": round(ms, 2),
+           "bwd_tflops": round(10 * w.d * w.Hq * P / (ms / 1e3) / 1e12, 2),
+           "two_kernel_bwd_ms": round(two_kernel_bwd_ms, 2),
+           "speed_vs_two_kernel": round(two_kernel_bwd_ms / ms, 3),
+           "nan_in_dq": bool(torch.isnan(dq.float()).any()),
+           "peak_hbm_gib": round((torch.cuda.max_memory_allocated(dev) - base) / GIB, 3),
+           "workspace_gib": round(ws_bytes / GIB, 3), "kernels": kernels,
+           "flops": "10*d*Hq*pairs (five products per pair, executed once)"}
+    print(f"[bench] fused backward: {ms:.1f} ms ({res['bwd_tflops']:.1f} TFLOP/s), two-kernel {two_kernel_bwd_ms:.1f} ms",
+          file=sys.stderr, flush=True)
+    del q, k, v, do, out, lse, out_lo, dq, dk, dv, ws
+    return res
+
+
 def roofline(w, res, head_chunk):
     """Roofline entry for the attention kernel with the most time per step."""
     attn = {n: e for n, e in res["kernels"].items() if n in ALGO_FLOPS_PER_PAIR_D}
@@ -460,6 +512,7 @@ def main():
     ap.add_argument("--sweep-warmup", type=int, default=1)
     ap.add_argument("--no-block", action="store_true",
                     help="skip the attention-block forward sweep (projections around the chunk loop)")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused deterministic backward leg")
     ap.add_argument("--no-loss", action="store_true", help="skip the sequence-tiled cross-entropy leg")
     ap.add_argument("--no-mlp", action="store_true", help="skip the sequence-tiled MLP leg")
     ap.add_argument("--no-residual-run", action="store_true",
@@ -519,6 +572,10 @@ def main():
                   "steps": 1, "warmup": 0}
         print(f"[bench] without out_lo: peak {r['peak_hbm_gib']:.2f} GiB", file=sys.stderr, flush=True)
 
+    fused = None
+    if not args.no_fused and w.dtype == "bf16" and w.d == 128 and not w.doc_lengths:
+        fused = fused_leg(w, hc, dev, res["bwd_ms"])
+
     block = None
     if not args.no_block and w.dtype == "bf16" and not w.doc_lengths:
         block = block_sweep(w, dev, list(w.head_chunks))
@@ -572,6 +629,8 @@ def main():
     }
     if sweep:
         line["head_chunk_sweep"] = sweep
+    if fused:
+        line["fused_backward"] = fused
     if block:
         line["block_fwd"] = block
     if loss_res:
