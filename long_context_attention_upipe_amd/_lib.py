@@ -55,11 +55,6 @@ def lib() -> ctypes.CDLL:
     L.upipe_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, sz,
                                  vp]
     L.upipe_attn_bwd.restype = i32
-    L.upipe_attn_bwd_fused_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
-    L.upipe_attn_bwd_fused_workspace_bytes.restype = sz
-    L.upipe_attn_bwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp,
-                                       sz, vp]
-    L.upipe_attn_bwd_fused.restype = i32
     L.upipe_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32, vp]
     L.upipe_attn_fwd_noalloc.restype = i32
     L.upipe_gemm_bf16.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, i32, i32, i32,
@@ -83,9 +78,9 @@ def lib() -> ctypes.CDLL:
     L.upipe_mlp_tiled_fwd.restype = i32
     L.upipe_mlp_tiled_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, vp, sz, vp]
     L.upipe_mlp_tiled_bwd.restype = i32
-    # The packed-document entry points are bound when the loaded build has
-    # them (UPIPE_ATTN_LIBRARY may name an older build); calling them on a
-    # build without them raises AttributeError.
+    # The packed-document and fused-backward entry points are bound when the
+    # loaded build has them (UPIPE_ATTN_LIBRARY may name an older build);
+    # calling them on a build without them raises AttributeError.
     if hasattr(L, "upipe_attn_fwd_docs"):
         L.upipe_attn_fwd_docs.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp, i32, i32, vp,
                                           sz, vp]
@@ -93,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.upipe_attn_bwd_docs.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, vp,
                                           i32, i32, vp, sz, vp]
         L.upipe_attn_bwd_docs.restype = i32
+    if hasattr(L, "upipe_attn_bwd_fused"):
+        L.upipe_attn_bwd_fused_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+        L.upipe_attn_bwd_fused_workspace_bytes.restype = sz
+        L.upipe_attn_bwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i32,
+                                           vp, sz, vp]
+        L.upipe_attn_bwd_fused.restype = i32
     p32 = ctypes.POINTER(ctypes.c_int32)
     L.upipe_attn_plan.argtypes = [i32, i32, i32, i32, p32, p32, p32, p32]
     L.upipe_attn_plan.restype = i32

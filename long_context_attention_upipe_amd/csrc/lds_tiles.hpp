@@ -201,13 +201,7 @@ __device__ __forceinline__ void tile_load_untracked(bf16* tile, const bf16* g, i
   constexpr int CPR = D / 8;
   constexpr int PER = ROWS * CPR / (64 * NWAVES);
   static_assert(ROWS * CPR == PER * 64 * NWAVES && (PER == 1 || PER == 2 || PER == 4), "1, 2 or 4 wave copies per wave");
-  // The base goes in SGPRs; readfirstlane (of each 32-bit half: the builtin
-  // takes an int) keeps it there even where the compiler cannot tell that it
-  // is the same in every lane.
-  const uint64_t b64 = (uint64_t)(uintptr_t)(g + (size_t)g_row0 * D);
-  const uint32_t b_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
-  const uint32_t b_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b64 >> 32));
-  const bf16* base = (const bf16*)(uintptr_t)(((uint64_t)b_hi << 32) | b_lo);
+  const bf16* base = g + (size_t)g_row0 * D;
   const int last = S - 1 - g_row0;  // rows past S - 1 repeat row S - 1
   unsigned o[PER];
 #pragma unroll
