@@ -94,6 +94,51 @@ __device__ __forceinline__ void gemm_load_tile(bf16* tile, const GemmOperand& op
   }
 }
 
+// Four 16-byte-per-lane global -> LDS copies from per-lane 64-bit addresses
+// to LDS l, l + STEP, l + 2 STEP, l + 3 STEP (bytes; M0 saved and restored),
+// issued from inline assembly so that the compiler does not track them: it
+// then does not wait for them before LDS reads of the other buffer. They
+// write no register; the caller waits for them by count (vmcnt) and a
+// barrier before the destination is read.
+template <unsigned STEP>
+__device__ __forceinline__ void gemm_copy16x4_untracked(const void* a0, const void* a1, const void* a2, const void* a3,
+                                                        lds_void* l) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)l);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_add_u32 m0, m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\t"
+      "s_add_u32 m0, m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, off\n\t"
+      "s_add_u32 m0, m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, off\n\t"
+      "s_nop 0\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "s"(m0), "i"(STEP)
+      : "memory", "scc");
+}
+
+// gemm_load_tile through the untracked copies: four copies per wave of a
+// 4-wave group (wave = 0..3 within the group).
+template <int KMAJOR, int MODE>
+__device__ __forceinline__ void gemm_load_tile_untracked(bf16* tile, const GemmOperand& op, int mn0, int MN, int k0,
+                                                         int wave, int lane) {
+  const void* a[4];
+#pragma unroll
+  for (int i0 = 0; i0 < 4; ++i0) {
+    const int i = i0 * 4 + wave, slot = i * 64 + lane;
+    if constexpr (KMAJOR) {
+      constexpr int D = 64, CPR = D / 8;
+      const int r = slot / CPR, pos = slot % CPR, c = pos ^ swz<D, MODE>(r);
+      a[i0] = gemm_elem(op, (int64_t)k0 + c * 8, min(mn0 + r, MN - 1));
+    } else {
+      constexpr int D = 128, CPR = D / 8;
+      const int r = slot / CPR, pos = slot % CPR, c = pos ^ swz<D, MODE>(r);
+      a[i0] = gemm_elem(op, min(mn0 + c * 8, MN - 8), min(k0 + r, op.kvalid - 1));
+    }
+  }
+  gemm_copy16x4_untracked<4 * 1024>(a[0], a[1], a[2], a[3], (lds_void*)(tile + wave * 512));
+}
+
 // Operand fragment for MFMA step ks (k = 16 ks .. 16 ks + 15 of the tile) and
 // the 32-row block mb of the operand's 128 M (or N) rows. NATURAL (both
 // operands k-major): lane half h supplies k = 8h .. 8h + 7, one 16-byte read.
@@ -177,6 +222,92 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams<CT> p) {
         const int n = n0 + (wn + j) * 32 + 8 * g + 4 * half;  // registers 4g .. 4g+3: n .. n+3
         if (n >= p.N) continue;
         const int sh = min(p.c.blk_shift, 31);  // n < 2^31: a shift of 31 leaves block 0
+        CT* dst = p.c.p + (int64_t)((unsigned)n >> sh) * p.c.blk_stride + (int64_t)m * p.c.ldc +
+                  ((unsigned)n & ((1u << sh) - 1u));
+        floatx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+        if constexpr (std::is_same<CT, float>::value) {
+          if (p.accumulate) {
+            const floatx4 old = *reinterpret_cast<const floatx4*>(dst);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = old[e] + v[e];
+          }
+          *reinterpret_cast<floatx4*>(dst) = v;
+        } else {
+          *reinterpret_cast<bf16x4*>(dst) = to_out4(v, bf16());
+        }
+      }
+  }
+}
+
+// The same product with a 256 x 256 C tile per workgroup of 8 waves (one
+// workgroup per CU), each wave 128 x 64 (4 x 2 MFMA tiles), for problems with
+// at least one such tile per CU. Each MFMA then reads 0.75 KiB of operands
+// from LDS instead of 1 KiB, and each operand tile is copied once for twice
+// the MFMAs. Operand tiles are two 128-row halves in the layout above (waves
+// 0-3 copy one half, 4-7 the other), double-buffered (128 KiB of LDS).
+template <typename CT, int AK, int BK>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_256_kernel(GemmParams<CT> p) {
+  constexpr int MODE = kSwzAll;
+  constexpr int NATURAL = AK && BK;
+  __shared__ __attribute__((aligned(1024))) bf16 sA[2][2][128 * 64];
+  __shared__ __attribute__((aligned(1024))) bf16 sB[2][2][128 * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.x * 256, n0 = blockIdx.y * 256;
+  const int wm = wave & 1;                         // this wave's 128-row half of M
+  const int nh = wave >> 2, nb0 = (wave >> 1) & 1;  // its 128-column half of N, and 64-column quarter in it
+  const int ch = wave >> 2, cw = wave & 3;         // the half this wave copies, its index among that half's 4 waves
+  const int nk = p.K / 64;
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+
+  gemm_load_tile<AK, MODE>(sA[0][ch], p.a, m0 + 128 * ch, p.M, 0, cw, lane);
+  gemm_load_tile<BK, MODE>(sB[0][ch], p.b, n0 + 128 * ch, p.N, 0, cw, lane);
+  wait_vm();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    // The next K tile's copies go out first, into the buffer the last step
+    // read before its closing barrier; the untracked copies let this step's
+    // fragment reads and MFMAs run while they fly.
+    if (kt + 1 < nk) {
+      gemm_load_tile_untracked<AK, MODE>(sA[cur ^ 1][ch], p.a, m0 + 128 * ch, p.M, (kt + 1) * 64, cw, lane);
+      gemm_load_tile_untracked<BK, MODE>(sB[cur ^ 1][ch], p.b, n0 + 128 * ch, p.N, (kt + 1) * 64, cw, lane);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = gemm_frag<AK, NATURAL, MODE>(sA[cur][wm], ks, i, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bfr[j] = gemm_frag<BK, NATURAL, MODE>(sB[cur][nh], ks, 2 * nb0 + j, lane);
+      // C^T tiles: lane = m (column of C^T), registers = n
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma32(acc[i][j], bfr[j], af[i]);
+    }
+    wait_vm();
+    __syncthreads();
+  }
+
+  const int half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 128 + i * 32 + (lane & 31);
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + nh * 128 + (2 * nb0 + j) * 32 + 8 * g + 4 * half;  // registers 4g .. 4g+3: n .. n+3
+        if (n >= p.N) continue;
+        const int sh = min(p.c.blk_shift, 31);
         CT* dst = p.c.p + (int64_t)((unsigned)n >> sh) * p.c.blk_stride + (int64_t)m * p.c.ldc +
                   ((unsigned)n & ((1u << sh) - 1u));
         floatx4 v;

@@ -675,6 +675,21 @@ int gemm(const GemmOperand& a, const GemmOperand& b, const GemmOut<CT>& c, int M
   p.N = N;
   p.K = K;
   p.accumulate = accumulate;
+  // 256 x 256 tiles (one 8-wave workgroup per CU) when there is at least one
+  // per CU; 128 x 128 tiles (two 4-wave workgroups per CU) otherwise.
+  const int64_t big_tiles = ((int64_t)M + 255) / 256 * (((int64_t)N + 255) / 256);
+  if (big_tiles >= 256) {
+    const dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 255) / 256));
+    if (a.kmajor && b.kmajor)
+      hipLaunchKernelGGL((gemm_bf16_256_kernel<CT, 1, 1>), grid, dim3(512), 0, st, p);
+    else if (a.kmajor)
+      hipLaunchKernelGGL((gemm_bf16_256_kernel<CT, 1, 0>), grid, dim3(512), 0, st, p);
+    else if (b.kmajor)
+      hipLaunchKernelGGL((gemm_bf16_256_kernel<CT, 0, 1>), grid, dim3(512), 0, st, p);
+    else
+      hipLaunchKernelGGL((gemm_bf16_256_kernel<CT, 0, 0>), grid, dim3(512), 0, st, p);
+    return check_launch("gemm");
+  }
   const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128));
   if (a.kmajor && b.kmajor)
     hipLaunchKernelGGL((gemm_bf16_kernel<CT, 1, 1>), grid, dim3(256), 0, st, p);

@@ -83,6 +83,57 @@ def test_gemm_blocked_operands_and_output_and_accumulate():
     assert np.abs(f64(C1) - ref1).max() <= 1e-5 * np.abs(ref1).max()
 
 
+@pytest.mark.parametrize("a_kmajor,b_kmajor", [(1, 1), (1, 0), (0, 1), (0, 0)])
+@pytest.mark.parametrize("c_dtype", [torch.float32, torch.bfloat16])
+def test_gemm_256_tiles_every_layout_and_same_sums_as_128_tiles(a_kmajor, b_kmajor, c_dtype):
+    """Problems with at least one 256 x 256 tile per CU take the 8-wave
+    kernel: every layout pair, ragged M and N, K over several steps, against
+    fp64; and, since both kernels add each C entry over K in the same order,
+    the first 256 rows equal (bit for bit) a 256-row product, which takes the
+    128 x 128 kernel."""
+    dev = _dev()
+    M, N, K = 4104, 4000, 320  # 17 x 16 tiles of 256
+    print(f"\n  gemm {M}x{N}x{K} a_kmajor={a_kmajor} b_kmajor={b_kmajor} {c_dtype}", flush=True)
+    A, B = _bf16((M, K), 11, dev), _bf16((N, K), 12, dev)
+    ta, la = _as_operand(A, a_kmajor)
+    tb, lb = _as_operand(B, b_kmajor)
+    C = torch.full((M, N), float("nan"), dtype=c_dtype, device=dev)
+    up.upipe_gemm_bf16(ta, la, tb, lb, C, {"ld": N}, M, N, K)
+    A_top = A[:256]
+    ta2, la2 = _as_operand(A_top, a_kmajor)
+    C2 = torch.full((256, N), float("nan"), dtype=c_dtype, device=dev)
+    up.upipe_gemm_bf16(ta2, la2, tb, lb, C2, {"ld": N}, 256, N, K)
+    torch.cuda.synchronize()
+    ref = f64(A) @ f64(B).T
+    rel = 1e-5 if c_dtype == torch.float32 else 5e-3
+    got = f64(C)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= rel * np.abs(ref).max()
+    assert bit_equal(C[:256], C2), "256 x 256 and 128 x 128 tiles sum differently"
+
+
+def test_gemm_256_tiles_blocked_operands_and_output_and_accumulate():
+    """The 8-wave kernel with blocked layouts (k-major A in 64-element blocks,
+    mn-major B in 128-element blocks, C written in 128-column blocks), M not a
+    multiple of 8, then C += A B on fp32 C."""
+    dev = _dev()
+    M, N, K = 4353, 3840, 256  # 18 x 15 tiles of 256
+    A, B = _bf16((M, K), 13, dev), _bf16((N, K), 14, dev, 0.1)
+    ta, la = _as_operand(A, 1, blk=64)
+    tb, lb = _as_operand(B, 0, blk=128)
+    C = torch.empty((N // 128, M, 128), dtype=torch.bfloat16, device=dev)
+    up.upipe_gemm_bf16(ta, la, tb, lb, C, {"ld": 128, "blk": 128, "blk_stride": M * 128}, M, N, K)
+    ref = f64(A) @ f64(B).T
+    got = f64(C.permute(1, 0, 2).reshape(M, N))
+    assert np.abs(got - ref).max() <= 5e-3 * np.abs(ref).max()
+    C0 = _bf16((M, N), 15, dev).float()
+    C1 = C0.clone()
+    up.upipe_gemm_bf16(ta, la, tb, lb, C1, {"ld": N}, M, N, K, accumulate=True)
+    torch.cuda.synchronize()
+    ref1 = f64(C0) + ref
+    assert np.abs(f64(C1) - ref1).max() <= 1e-5 * np.abs(ref1).max()
+
+
 def test_gemm_rejects_bad_layouts():
     dev = _dev()
     A, B = _bf16((64, 100), 6, dev), _bf16((64, 100), 7, dev)
