@@ -58,6 +58,8 @@ struct GemmParams {
   GemmOut<CT> c;
   int M, N, K;     // K a multiple of 64; M, N, block lengths multiples of 8
   int accumulate;  // fp32 C only: C += A B (else C = A B)
+  int k_split;     // 0, or the K range (a multiple of 64) of each blockIdx.z: that range's
+  float* partial;  // product goes to partial + z * M * N, fp32 [M][N], instead of C
 };
 
 __device__ __forceinline__ const bf16* gemm_elem(const GemmOperand& op, int64_t c, int64_t o) {
@@ -173,7 +175,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams<CT> p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.x * 128, n0 = blockIdx.y * 128;
   const int wm = (wave & 1) * 2, wn = (wave >> 1) * 2;  // this wave's 32-row blocks of M and of N
-  const int nk = p.K / 64;
+  const int kb = p.k_split ? (int)blockIdx.z * p.k_split : 0;  // this workgroup's K range
+  const int nk = (p.k_split ? min(p.k_split, p.K - kb) : p.K) / 64;
 
   floatx16 acc[2][2];
 #pragma unroll
@@ -181,8 +184,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams<CT> p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
 
-  gemm_load_tile<AK, MODE>(sA[0], p.a, m0, p.M, 0, wave, lane);
-  gemm_load_tile<BK, MODE>(sB[0], p.b, n0, p.N, 0, wave, lane);
+  gemm_load_tile<AK, MODE>(sA[0], p.a, m0, p.M, kb, wave, lane);
+  gemm_load_tile<BK, MODE>(sB[0], p.b, n0, p.N, kb, wave, lane);
   wait_vm();
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
@@ -196,8 +199,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams<CT> p) {
         bfr[ks][i] = gemm_frag<BK, NATURAL, MODE>(sB[cur], ks, wn + i, lane);
       }
     if (kt + 1 < nk) {
-      gemm_load_tile<AK, MODE>(sA[cur ^ 1], p.a, m0, p.M, (kt + 1) * 64, wave, lane);
-      gemm_load_tile<BK, MODE>(sB[cur ^ 1], p.b, n0, p.N, (kt + 1) * 64, wave, lane);
+      gemm_load_tile<AK, MODE>(sA[cur ^ 1], p.a, m0, p.M, kb + (kt + 1) * 64, wave, lane);
+      gemm_load_tile<BK, MODE>(sB[cur ^ 1], p.b, n0, p.N, kb + (kt + 1) * 64, wave, lane);
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
@@ -221,6 +224,13 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams<CT> p) {
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + (wn + j) * 32 + 8 * g + 4 * half;  // registers 4g .. 4g+3: n .. n+3
         if (n >= p.N) continue;
+        if (p.k_split) {
+          floatx4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+          *reinterpret_cast<floatx4*>(p.partial + ((size_t)blockIdx.z * p.M + m) * p.N + n) = v;
+          continue;
+        }
         const int sh = min(p.c.blk_shift, 31);  // n < 2^31: a shift of 31 leaves block 0
         CT* dst = p.c.p + (int64_t)((unsigned)n >> sh) * p.c.blk_stride + (int64_t)m * p.c.ldc +
                   ((unsigned)n & ((1u << sh) - 1u));
@@ -238,6 +248,27 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmParams<CT> p) {
           *reinterpret_cast<bf16x4*>(dst) = to_out4(v, bf16());
         }
       }
+  }
+}
+
+// C (+)= the sum of n_split fp32 partial products [z][M][N], added in
+// ascending z, written in C's layout (bf16: rounded once, at the end).
+template <typename CT>
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(const float* __restrict__ partial, int n_split, int M,
+                                                                int N, GemmOut<CT> c, int accumulate) {
+  const size_t n4 = (size_t)M * N / 4;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i * 4 / N), n = (int)(i * 4 % N);
+    floatx4 v = *reinterpret_cast<const floatx4*>(partial + i * 4);
+    for (int z = 1; z < n_split; ++z) v += *reinterpret_cast<const floatx4*>(partial + (size_t)z * M * N + i * 4);
+    const int sh = min(c.blk_shift, 31);
+    CT* dst = c.p + (int64_t)((unsigned)n >> sh) * c.blk_stride + (int64_t)m * c.ldc + ((unsigned)n & ((1u << sh) - 1u));
+    if constexpr (std::is_same<CT, float>::value) {
+      if (accumulate) v += *reinterpret_cast<const floatx4*>(dst);
+      *reinterpret_cast<floatx4*>(dst) = v;
+    } else {
+      *reinterpret_cast<bf16x4*>(dst) = to_out4(v, bf16());
+    }
   }
 }
 

@@ -675,6 +675,8 @@ int gemm(const GemmOperand& a, const GemmOperand& b, const GemmOut<CT>& c, int M
   p.N = N;
   p.K = K;
   p.accumulate = accumulate;
+  p.k_split = 0;
+  p.partial = nullptr;
   // 256 x 256 tiles (one 8-wave workgroup per CU) when there is at least one
   // per CU; 128 x 128 tiles (two 4-wave workgroups per CU) otherwise.
   const int64_t big_tiles = ((int64_t)M + 255) / 256 * (((int64_t)N + 255) / 256);
@@ -700,6 +702,53 @@ int gemm(const GemmOperand& a, const GemmOperand& b, const GemmOut<CT>& c, int M
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<CT, 0, 0>), grid, dim3(256), 0, st, p);
   return check_launch("gemm");
+}
+
+// The same product with K split into ranges of k_split (a multiple of 64):
+// one workgroup per (128 x 128 tile, range) writes its fp32 partial product
+// to `partial` ([ranges][M][N]), and a second kernel adds the ranges in
+// ascending order into C (C += when accumulate). For products with few tiles
+// and a long K (the weight gradients, contracted over every token).
+template <typename CT>
+int gemm_split(const GemmOperand& a, const GemmOperand& b, const GemmOut<CT>& c, int M, int N, int K, int k_split,
+               int accumulate, float* partial, hipStream_t st) {
+  GemmParams<CT> p;
+  p.a = a;
+  p.b = b;
+  p.c = c;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.accumulate = 0;
+  p.k_split = k_split;
+  p.partial = partial;
+  const int n_split = (K + k_split - 1) / k_split;
+  const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128), (unsigned)n_split);
+  if (a.kmajor && b.kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<CT, 1, 1>), grid, dim3(256), 0, st, p);
+  else if (a.kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<CT, 1, 0>), grid, dim3(256), 0, st, p);
+  else if (b.kmajor)
+    hipLaunchKernelGGL((gemm_bf16_kernel<CT, 0, 1>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<CT, 0, 0>), grid, dim3(256), 0, st, p);
+  hipLaunchKernelGGL((gemm_split_reduce_kernel<CT>), dim3(copy_grid((size_t)M * N / 4)), dim3(256), 0, st, partial,
+                     n_split, M, N, c, accumulate);
+  return check_launch("split gemm");
+}
+
+// How the token-contracting products split their K = S rows (whole 64-row
+// steps): up to 64 ranges of at least 8192 tokens, a function of S alone, so
+// every head_chunk adds each weight gradient's terms in the same order.
+struct TokenSplit {
+  int k_split, n_split;  // n_split < 2: no split
+};
+TokenSplit token_split(int64_t S) {
+  const int64_t K0 = S / 64 * 64;
+  const int64_t n = std::min<int64_t>(64, K0 / 8192);
+  if (n < 2) return {0, 1};
+  const int64_t k = (K0 / n + 63) / 64 * 64;
+  return {(int)k, (int)((K0 + k - 1) / k)};
 }
 
 // ---------------------------------------------------------------------------
@@ -812,7 +861,7 @@ int run_block_fwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
 // rounding residual and the recomputed lse. Every chunk reuses the offsets.
 // ---------------------------------------------------------------------------
 struct BlockBwdPool {
-  size_t q, o, dout, dq, k, v, dk, dv, neg_d, lse2, dk_acc, dv_acc, xtail, dytail, vt, olo, lrec, total;
+  size_t q, o, dout, dq, k, v, dk, dv, neg_d, lse2, dk_acc, dv_acc, xtail, dytail, vt, olo, lrec, split, total;
   bool has_acc;
 };
 BlockBwdPool block_bwd_pool(const Problem& pr, int Dm, bool recompute) {
@@ -839,6 +888,9 @@ BlockBwdPool block_bwd_pool(const Problem& pr, int Dm, bool recompute) {
   p.vt = off; off += recompute ? align_up(pr.nkv * vt_bytes(pr)) : 0;
   p.olo = off; off += recompute ? align_up(pr.hc * U) : 0;
   p.lrec = off; off += recompute ? align_up(R) : 0;
+  // fp32 partial products of the split weight-gradient GEMMs (the largest is hc*d x Dm)
+  const TokenSplit ts = token_split(pr.S);
+  p.split = off; off += ts.n_split > 1 ? align_up((size_t)ts.n_split * pr.hc * pr.d * Dm * 4) : 0;
   p.total = off;
   return p;
 }
@@ -850,9 +902,13 @@ BlockBwdPool block_bwd_pool(const Problem& pr, int Dm, bool recompute) {
 // `a_tail` is A advanced by K0 tokens.
 template <typename CT>
 int gemm_over_tokens(const GemmOperand& a, const GemmOperand& a_tail, const GemmOperand& b, const GemmOperand& b_tail,
-                     const GemmOut<CT>& c, int M, int N, int S, hipStream_t st) {
+                     const GemmOut<CT>& c, int M, int N, int S, float* split_buf, hipStream_t st) {
   const int K0 = S / 64 * 64;
-  if (K0 > 0) timed(K_GEMM, st, [&] { (void)gemm(a, b, c, M, N, K0, 0, st); });
+  const TokenSplit ts = token_split(S);
+  if (K0 > 0 && ts.n_split > 1)
+    timed(K_GEMM, st, [&] { (void)gemm_split(a, b, c, M, N, K0, ts.k_split, 0, split_buf, st); });
+  else if (K0 > 0)
+    timed(K_GEMM, st, [&] { (void)gemm(a, b, c, M, N, K0, 0, st); });
   if (S > K0) timed(K_GEMM, st, [&] { (void)gemm(a_tail, b_tail, c, M, N, 64, K0 > 0, st); });
   return check_launch("gemm over tokens");
 }
@@ -883,6 +939,7 @@ int run_block_bwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
   bf16* Vt = recompute ? reinterpret_cast<bf16*>(ws + pool.vt) : nullptr;
   bf16* OLc = recompute ? reinterpret_cast<bf16*>(ws + pool.olo) : nullptr;
   float* Lrec = recompute ? reinterpret_cast<float*>(ws + pool.lrec) : nullptr;
+  float* split_buf = reinterpret_cast<float*>(ws + pool.split);
   const bf16* xb = reinterpret_cast<const bf16*>(x);
   const bf16* dyb = reinterpret_cast<const bf16*>(dy);
   const int n_fwd_tiles = (S + Bf16Tiles::kFwdRows - 1) / Bf16Tiles::kFwdRows;
@@ -1002,22 +1059,22 @@ int run_block_bwd(const Problem& pr, int Dm, const void* x, const void* wq, cons
     // dWo's columns of the chunk's heads = dy^T o: [M = Dm][N = hc*D], K = tokens
     const GemmOperand o_tok = operand(Oc, D, 0, D, SD), o_tail = operand(Oc + (int64_t)K0 * D, D, 0, D, SD, tail);
     if (int rc = gemm_over_tokens(dy_tok, dy_tail, o_tok, o_tail, gemm_out(dwo + (int64_t)c.q_head0 * D,
-                                  (int64_t)pr.Hq * D), Dm, pr.hc * D, S, st))
+                                  (int64_t)pr.Hq * D), Dm, pr.hc * D, S, split_buf, st))
       return rc;
     // dWq rows of the chunk's heads = dq^T x: [M = hc*D][N = Dm]
     const GemmOperand dq_tok = operand(dQc, D, 0, D, SD), dq_tail = operand(dQc + (int64_t)K0 * D, D, 0, D, SD, tail);
     if (int rc = gemm_over_tokens(dq_tok, dq_tail, x_tok, x_tail, gemm_out(dwq + (int64_t)c.q_head0 * D * Dm,
-                                  (int64_t)Dm), pr.hc * D, Dm, S, st))
+                                  (int64_t)Dm), pr.hc * D, Dm, S, split_buf, st))
       return rc;
     if (c.last_for_kv) {
       const int64_t ldk = (int64_t)c.n_kv * D;  // dk, dv rows: [S][nkv][D]
       const GemmOperand dk_tok = operand(dKc, ldk, 0), dk_tail = operand(dKc + K0 * ldk, ldk, 0, kUnblocked, 0, tail);
       const GemmOperand dv_tok = operand(dVc, ldk, 0), dv_tail = operand(dVc + K0 * ldk, ldk, 0, kUnblocked, 0, tail);
       if (int rc = gemm_over_tokens(dk_tok, dk_tail, x_tok, x_tail,
-                                    gemm_out(dwk + (int64_t)c.kv_head0 * D * Dm, (int64_t)Dm), c.n_kv * D, Dm, S, st))
+                                    gemm_out(dwk + (int64_t)c.kv_head0 * D * Dm, (int64_t)Dm), c.n_kv * D, Dm, S, split_buf, st))
         return rc;
       if (int rc = gemm_over_tokens(dv_tok, dv_tail, x_tok, x_tail,
-                                    gemm_out(dwv + (int64_t)c.kv_head0 * D * Dm, (int64_t)Dm), c.n_kv * D, Dm, S, st))
+                                    gemm_out(dwv + (int64_t)c.kv_head0 * D * Dm, (int64_t)Dm), c.n_kv * D, Dm, S, split_buf, st))
         return rc;
     }
     // dx (+)= dq_h Wq_h for the chunk's heads of each kv group, then, once

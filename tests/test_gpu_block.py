@@ -254,6 +254,9 @@ def _check_grads(got, refs):
     (1000, 192, 8, 2, 64, (1, 2, 4, 8), True),
     (517, 256, 4, 2, 128, (1, 4), False),
     (8192, 256, 4, 1, 128, (1, 4), True),
+    # 20,000 tokens: the weight gradients' token contraction runs split in two
+    # ranges (added in order by a second kernel), then the 32-token tail
+    (20000, 128, 2, 1, 64, (1, 2), True),
 ])
 def test_block_backward_full(S, Dm, Hq, Hkv, d, hcs, causal):
     """dx and the four weight gradients against the oracle at every element,
