@@ -310,18 +310,43 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_256_kernel(GemmParams<CT> p)
       gemm_load_tile_untracked<AK, MODE>(sA[cur ^ 1][ch], p.a, m0 + 128 * ch, p.M, (kt + 1) * 64, cw, lane);
       gemm_load_tile_untracked<BK, MODE>(sB[cur ^ 1][ch], p.b, n0 + 128 * ch, p.N, (kt + 1) * 64, cw, lane);
     }
+    if constexpr (!AK && !BK) {
+      // Both operands read transposed (two 8-byte reads per fragment): the
+      // fragments of step ks + 1 are read while step ks's MFMAs run.
+      bf16x8 af[2][4], bfr[2][2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 af[4], bfr[2];
+      for (int i = 0; i < 4; ++i) af[0][i] = gemm_frag<AK, NATURAL, MODE>(sA[cur][wm], 0, i, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = gemm_frag<AK, NATURAL, MODE>(sA[cur][wm], ks, i, lane);
+      for (int j = 0; j < 2; ++j) bfr[0][j] = gemm_frag<BK, NATURAL, MODE>(sB[cur][nh], 0, 2 * nb0 + j, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = gemm_frag<BK, NATURAL, MODE>(sB[cur][nh], ks, 2 * nb0 + j, lane);
-      // C^T tiles: lane = m (column of C^T), registers = n
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c = ks & 1;
+        if (ks + 1 < 4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) af[c ^ 1][i] = gemm_frag<AK, NATURAL, MODE>(sA[cur][wm], ks + 1, i, lane);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma32(acc[i][j], bfr[j], af[i]);
+          for (int j = 0; j < 2; ++j)
+            bfr[c ^ 1][j] = gemm_frag<BK, NATURAL, MODE>(sB[cur][nh], ks + 1, 2 * nb0 + j, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) mma32(acc[i][j], bfr[c][j], af[c][i]);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 af[4], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = gemm_frag<AK, NATURAL, MODE>(sA[cur][wm], ks, i, lane);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bfr[j] = gemm_frag<BK, NATURAL, MODE>(sB[cur][nh], ks, 2 * nb0 + j, lane);
+        // C^T tiles: lane = m (column of C^T), registers = n
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) mma32(acc[i][j], bfr[j], af[i]);
+      }
     }
     wait_vm();
     __syncthreads();
