@@ -18,10 +18,12 @@
 //    reader on that XCD whose load skips its CU's L1 (sc0), and no L2
 //    write-back is needed;
 //  * the tiles of an XCD are handed out by a per-XCD ticket counter in
-//    ascending kt (the heaviest causal tiles first), and the tile kt adds its
-//    32-row slice of a row block only after tile kt - nx has added its own:
-//    per wave (each wave owns 32 of the 128 dQ columns) a progress word
-//    counts the steps whose additions have completed;
+//    ascending kt (the heaviest causal tiles first), and tile kt adds its
+//    terms to a 32-row block only after tile kt - nx has added its own: per
+//    wave (each wave owns 32 of the 128 dQ columns) a progress word counts
+//    the steps whose additions have completed, stored once those stores have
+//    completed (into the XCD's L2) and read by the next tile through the
+//    scalar unit with the scalar cache bypassed;
 //  * a final kernel adds the nx partials in ascending x.
 // The tile a workgroup waits for holds an earlier ticket of the same queue,
 // so it was taken by a workgroup that is already running: the lowest
