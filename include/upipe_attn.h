@@ -20,8 +20,10 @@
  * head_chunk heads; every chunk reuses the same buffers of one fixed pool
  * (the workspace) instead of allocating buffers for all heads at once (talk
  * summary, Chapters: the chapter on processing heads in batches; talk digest,
- * Quiz answer on U-Pipe). Peak device memory therefore grows with head_chunk,
- * not with Hq. Per chunk: the chunk's heads are copied from the caller's
+ * Quiz answer on U-Pipe). Peak device memory is therefore set by head_chunk,
+ * not by Hq. It grows with head_chunk, with one exception: a chunk that holds
+ * a whole kv group needs no fp32 dK/dV accumulators, so at Hq/Hkv = 2 in bf16
+ * the backward pool is smaller at head_chunk 2 than at 1. Per chunk: the chunk's heads are copied from the caller's
  * token-major tensors into head-major pool buffers (the single-GPU stand-in
  * for the Ulysses all-to-all), the attention kernels run on the pool, and the
  * results are copied back.
@@ -106,8 +108,9 @@ size_t upipe_attn_workspace_bytes(int64_t S, int Hq, int Hkv, int d,
  * talk digest, Plan: pick the chunk from the memory left): returns the
  * largest valid head_chunk whose workspace (upipe_attn_workspace_bytes) fits
  * in budget_bytes -- larger chunks take fewer, wider launches and more
- * memory. Host only. Returns UPIPE_EWORKSPACE if even head_chunk 1 does not
- * fit, or another negative status for invalid arguments.
+ * memory. Every valid head_chunk is considered (pools are not monotone in
+ * head_chunk, see above). Host only. Returns UPIPE_EWORKSPACE if no valid
+ * head_chunk fits, or another negative status for invalid arguments.
  */
 int upipe_attn_pick_head_chunk(int64_t S, int Hq, int Hkv, int d, int dtype,
                                size_t budget_bytes);

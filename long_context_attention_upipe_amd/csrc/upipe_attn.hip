@@ -7,7 +7,7 @@
 // fills the GPU, so the GPU's heads run as sequential chunks and every chunk
 // reuses the buffers the previous chunk used. Here the buffers are one
 // caller-provided workspace carved at fixed offsets; nothing is allocated
-// inside the chunk loop, and peak memory grows with head_chunk only.
+// inside the chunk loop, and peak memory depends on head_chunk, not on Hq.
 
 #include <hip/hip_runtime.h>
 
@@ -1314,16 +1314,23 @@ size_t upipe_attn_bwd_fused_workspace_bytes(int64_t S, int Hq, int Hkv, int d, i
 int upipe_attn_pick_head_chunk(int64_t S, int Hq, int Hkv, int d, int dtype, size_t budget_bytes) {
   Problem pr;
   if (int rc = validate(S, Hq, Hkv, d, 1, 1, dtype, &pr)) return rc;
-  int best = 0;
-  size_t need1 = 0;
+  // Every valid chunk size is tried: the pools are not monotone in hc (a
+  // chunk of a whole kv group drops the fp32 dK/dV accumulators, so at G = 2
+  // in bf16 head_chunk 2 needs less than 1).
+  int best = 0, min_hc = 0;
+  size_t min_need = 0;
   for (int hc = 1; hc <= Hq; ++hc) {
     if (validate(S, Hq, Hkv, d, hc, 1, dtype, &pr) != UPIPE_OK) continue;  // not a valid chunk size
     const size_t need = std::max(fwd_pool(pr).total, bwd_pool(pr).total);
-    if (hc == 1) need1 = need;
-    if (need <= budget_bytes) best = hc;  // pools grow strictly with hc: the last fit is the largest
+    if (!min_hc || need < min_need) {
+      min_hc = hc;
+      min_need = need;
+    }
+    if (need <= budget_bytes) best = hc;
   }
   if (!best)
-    return fail(UPIPE_EWORKSPACE, "even head_chunk 1 needs %zu workspace bytes, budget %zu", need1, budget_bytes);
+    return fail(UPIPE_EWORKSPACE, "no head_chunk fits: the smallest workspace is %zu bytes (head_chunk %d), budget %zu",
+                min_need, min_hc, budget_bytes);
   g_error.clear();
   return best;
 }

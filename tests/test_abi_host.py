@@ -255,7 +255,7 @@ def test_pick_head_chunk_takes_the_largest_pool_that_fits():
     sizes6 = {hc: L.upipe_attn_workspace_bytes(4096, 6, 2, 64, hc, 0) for hc in (1, 3, 6)}
     assert L.upipe_attn_pick_head_chunk(4096, 6, 2, 64, 0, sizes6[3] + 100) == 3
     assert L.upipe_attn_pick_head_chunk(4096, 6, 2, 64, 0, sizes6[6] - 1) == 3
-    with pytest.raises(L.UpipeError, match="even head_chunk 1"):
+    with pytest.raises(L.UpipeError, match="no head_chunk fits"):
         L.upipe_attn_pick_head_chunk(S, Hq, Hkv, d, 0, sizes[1] - 1)
     with pytest.raises(L.UpipeError, match="head dim"):
         L.upipe_attn_pick_head_chunk(S, Hq, Hkv, 96, 0, 1 << 50)
