@@ -330,9 +330,11 @@ def rows_forward_dq(q_rows, k, v, dout_rows, rows, causal: bool = True, doc_offs
 
 
 def cols_rows_needed(cols, S: int, causal: bool = True, doc_offsets=None) -> np.ndarray:
-    """The query rows whose softmax rows reach any of the keys ``cols``: from
-    the first key on when causal (from 0 otherwise), narrowed to the keys'
-    documents when the sequence is packed. Sorted positions."""
+    """The contiguous range of query rows from the first to the last row whose
+    softmax reaches any of the keys ``cols``: from the first key on when causal
+    (from 0 otherwise), narrowed to the keys' documents when the sequence is
+    packed. Rows inside the range that reach none of the keys (possible with
+    packed documents) add nothing to those keys' gradients. Sorted positions."""
     cols = np.asarray(cols, dtype=np.int64)
     bounds = _bounds(doc_offsets, S)
     first = int(cols.min()) if causal else 0
