@@ -360,7 +360,10 @@ int upipe_attn_block_bwd(const void* x, const void* wq, const void* wk, const vo
  *   G_ij   = grad_scale * (exp(z_ij - lse_i) - [j == label_i])   (bf16)
  *   dh_i   = sum_j G_ij W_j,   dw_j = sum_i G_ij h_i  (tile by tile, in order)
  *   h      [S, Dm] bf16 (final hidden states), w [V, Dm] bf16 (torch Linear
- *          layout), labels [S] int32 (negative: ignored)
+ *          layout), labels [S] int32 (negative: ignored; a label >= V is an
+ *          error the host cannot see: that token's loss is NaN and, with
+ *          gradients, so are its dh row and all of dw; nothing is read out
+ *          of bounds)
  *   loss   [S] fp32, natural log
  *   dh     [S, Dm] bf16 or NULL; dw [V, Dm] fp32 or NULL (written, not
  *          accumulated into); both NULL: forward only (no gradient buffer)

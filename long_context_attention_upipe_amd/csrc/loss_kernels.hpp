@@ -25,7 +25,9 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 // of `logits` (V fp32 values, row stride ldl); writes loss[r] = lse(z) -
 // z[label] (natural log; 0 for a label < 0, which is ignored) and, when G is
 // set, G[r][j] = bf16(scale * (exp(z_j - lse) - [j == label])) for j < V and
-// 0 for V <= j < ldg (0 across the row for an ignored label). Rows T <= r <
+// 0 for V <= j < ldg (0 across the row for an ignored label). A label >= V
+// names no logit: nothing is read for it, and the row's loss and its G
+// values j < V are NaN, so the error shows in loss, dh and dW. Rows T <= r <
 // gridDim.x write a zero G row (the backward GEMMs read whole 64-row tiles).
 // The reduction order is fixed, so results are deterministic.
 __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ logits, int ldl,
@@ -41,6 +43,7 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
   }
   const float* z = logits + (size_t)r * ldl;
   const int label = labels[r];
+  const bool bad_label = label >= V;
   // pass 1: per-thread online (max, sum) over 4-wide slices, then the waves, then the workgroup
   float m = -__builtin_inff(), s = 0.f;
   for (int j = tid * 4; j < V; j += 256 * 4) {
@@ -64,12 +67,12 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
     for (int w = 1; w < 4; ++w) lse_merge(mm, sm, red_m[w], red_s[w]);
     const float lse = mm + __logf(sm);
     s_lse = lse;
-    loss[r] = label >= 0 ? lse - z[label] : 0.f;
+    loss[r] = bad_label ? __builtin_nanf("") : label >= 0 ? lse - z[label] : 0.f;
   }
   __syncthreads();
   if (!g) return;
   const float lse = s_lse;
-  const float sc = label >= 0 ? scale : 0.f;
+  const float sc = bad_label ? __builtin_nanf("") : label >= 0 ? scale : 0.f;
   // pass 2: the gradient row, 8 values (16 bytes of bf16) per thread and step
   for (int j = tid * 8; j < ldg; j += 256 * 8) {
     bf16x8 out;

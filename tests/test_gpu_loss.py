@@ -77,3 +77,28 @@ def test_tiled_cross_entropy_tile_size_changes_only_dw_order():
     c = _run(h, w, labels, 256, 1e-3)
     for x, y in zip(a, c):
         assert bit_equal(x, y), "repeated call differs"
+
+
+def test_label_out_of_range_poisons_its_row_and_nothing_else():
+    """A label >= V names no logit. The kernel reads nothing for it: that
+    token's loss is NaN, and so are its dh row and (as dW sums over every
+    token) all of dW. Every other token's loss and dh row are bit-identical
+    to a call with that token's label ignored."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda:0")
+    S, Dm, V, tile = 300, 128, 1000, 128
+    h, w, labels = _inputs(S, Dm, V, 11, dev)
+    bad, ignored = labels.clone(), labels.clone()
+    for r in (0, 130, 299):  # first row, a row of the second tile, the last row of the ragged tile
+        bad[r] = V + 3 * r
+        ignored[r] = -100
+    print(f"\n  S={S} V={V}: labels out of range at rows 0, 130, 299", flush=True)
+    loss_b, dh_b, dw_b = _run(h, w, bad, tile, 1e-2)
+    loss_i, dh_i, _ = _run(h, w, ignored, tile, 1e-2)
+    rows = torch.tensor([0, 130, 299], device=dev)
+    keep = torch.ones(S, dtype=torch.bool, device=dev)
+    keep[rows] = False
+    assert bool(torch.isnan(loss_b[rows]).all()) and bool(torch.isnan(dh_b[rows].float()).all())
+    assert bool(torch.isnan(dw_b).all())
+    assert bit_equal(loss_b[keep], loss_i[keep]) and bit_equal(dh_b[keep], dh_i[keep])
