@@ -145,7 +145,7 @@ class OracleJobs:
 
     Every BLAS call is held to ONE thread while the pool runs: OpenBLAS
     (pthreads build) called concurrently from several threads, each running
-    its own multi-threaded GEMMs, returned wrong products on the GPU machine's
+    its own multi-threaded GEMMs, returned wrong products on a 16-core EPYC
     host (a full-tensor oracle run per head in 4 threads x 4 BLAS threads
     differed from the per-row oracle on 13,196 of 131,072 rows, on different
     rows from run to run), while single-threaded calls from many threads gave
