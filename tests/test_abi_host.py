@@ -409,3 +409,48 @@ def test_fused_backward_host_checks():
     assert call(ws=16) == -3 and "workspace too small" in L.upipe_last_error()
     assert call(hc=3) == -1 and "must divide Hq" in L.upipe_last_error()
     assert call(causal=2) == -1
+
+
+def _c_declarations():
+    """(name, return type, [parameter types]) of every function the header
+    declares, comments removed, whitespace normalised."""
+    with open(HEADER) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    out = []
+    for ret, name, params in re.findall(r"([A-Za-z_][\w\s\*]*?)\b(upipe_\w+)\s*\(([^;{]*?)\)\s*;", src, flags=re.S):
+        ps = [" ".join(p.split()) for p in params.split(",")] if params.strip() not in ("", "void") else []
+        # drop the parameter name: the type is everything before the last identifier
+        types = [re.sub(r"\s*\b\w+$", "", p) for p in ps]
+        out.append((name, " ".join(ret.split()), types))
+    return out
+
+
+def _ctype_matches(c_type, ct):
+    if c_type.endswith("*"):
+        # any pointer: void*, POINTER(...) or a char* string
+        return ct in (ctypes.c_void_p, ctypes.c_char_p) or (isinstance(ct, type) and issubclass(ct, ctypes._Pointer))
+    plain = {"int64_t": ctypes.c_int64, "int": ctypes.c_int, "size_t": ctypes.c_size_t, "float": ctypes.c_float,
+             "double": ctypes.c_double}
+    return ct is plain[c_type]
+
+
+def test_bindings_match_the_header_parameter_by_parameter():
+    """Every declared function is bound with as many arguments as the header
+    gives it, each of the same kind (pointer, int64_t, int, size_t, float),
+    and the same kind of result: a binding that drifted from the header would
+    pass its arguments in the wrong registers without any error."""
+    lib = L.lib()
+    decls = _c_declarations()
+    assert len(decls) == len(declared_functions())
+    for name, ret, params in decls:
+        fn = getattr(lib, name)
+        assert fn.argtypes is not None, f"{name}: no argtypes bound"
+        assert len(fn.argtypes) == len(params), f"{name}: {len(fn.argtypes)} bound arguments, header has {len(params)}"
+        for i, (c_type, ct) in enumerate(zip(params, fn.argtypes)):
+            assert _ctype_matches(c_type, ct), f"{name} argument {i}: header {c_type!r}, bound {ct}"
+        if ret == "void":
+            assert fn.restype is None, name
+        else:
+            assert _ctype_matches(ret, fn.restype), f"{name} result: header {ret!r}, bound {fn.restype}"
