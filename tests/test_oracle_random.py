@@ -49,7 +49,7 @@ def _allowed(S, causal, docs):
     return _doc_allowed(S, docs, causal)
 
 
-@settings(max_examples=150, deadline=None)
+@settings(max_examples=150, deadline=None, derandomize=True)
 @given(cases())
 def test_full_tensor_oracle_matches_torch_sdpa_and_autograd(c):
     S, Hq, Hkv, d, causal, block, docs, seed = c
@@ -76,7 +76,7 @@ def test_full_tensor_oracle_matches_torch_sdpa_and_autograd(c):
     np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-9, atol=1e-11)
 
 
-@settings(max_examples=150, deadline=None)
+@settings(max_examples=150, deadline=None, derandomize=True)
 @given(cases(), st.data())
 def test_row_and_key_functions_match_the_full_tensor_oracle(c, data):
     S, Hq, Hkv, d, causal, block, docs, seed = c

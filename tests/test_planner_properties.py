@@ -37,7 +37,7 @@ def valid_chunks(Hq, Hkv):
     return [hc for hc in range(1, Hq + 1) if rule(Hq, Hkv, hc)]
 
 
-@settings(max_examples=500, deadline=None)
+@settings(max_examples=500, deadline=None, derandomize=True)
 @given(Hq=st.integers(1, 48), Hkv=st.integers(1, 48), hc=st.integers(0, 50))
 def test_plan_accepts_exactly_the_rule_and_keeps_the_accumulation_contract(Hq, Hkv, hc):
     if not rule(Hq, Hkv, hc):
@@ -103,7 +103,7 @@ def layout_pools(S, Hq, Hkv, d, hc, dtype):
     return fwd, bwd
 
 
-@settings(max_examples=300, deadline=None)
+@settings(max_examples=300, deadline=None, derandomize=True)
 @given(problems())
 def test_pools_match_the_layout_and_workspace_is_their_max(p):
     S, Hq, Hkv, d, dtype = p
@@ -114,7 +114,7 @@ def test_pools_match_the_layout_and_workspace_is_their_max(p):
         assert L.upipe_attn_workspace_bytes(S, Hq, Hkv, d, hc, dtype) == max(fwd, bwd)
 
 
-@settings(max_examples=200, deadline=None)
+@settings(max_examples=200, deadline=None, derandomize=True)
 @given(problems())
 def test_pools_grow_with_head_chunk_except_where_the_accumulators_drop_out(p):
     """Each step up in head_chunk adds per-head buffers; the one saving is the
@@ -138,7 +138,7 @@ def test_pools_grow_with_head_chunk_except_where_the_accumulators_drop_out(p):
             assert bwd[i] > bwd[i - 1] if big else bwd[i] >= bwd[i - 1], (hcs, bwd)
 
 
-@settings(max_examples=200, deadline=None)
+@settings(max_examples=200, deadline=None, derandomize=True)
 @given(problems(), st.floats(0.0, 1.3))
 def test_pick_head_chunk_is_the_largest_that_fits(p, frac):
     S, Hq, Hkv, d, dtype = p
@@ -156,7 +156,7 @@ def test_pick_head_chunk_is_the_largest_that_fits(p, frac):
     assert L.upipe_attn_pick_head_chunk(S, Hq, Hkv, d, dtype, budget) == max(fits)
 
 
-@settings(max_examples=200, deadline=None)
+@settings(max_examples=200, deadline=None, derandomize=True)
 @given(problems())
 def test_fused_pool_is_the_two_kernel_pool_without_dq_plus_the_partials(p):
     S, Hq, Hkv, _, _ = p
